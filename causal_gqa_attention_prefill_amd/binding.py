@@ -1,0 +1,166 @@
+"""Python binding of libprefill_attn.so (ctypes; argument marshalling only).
+
+Every step of the attention runs in the HIP kernels of the library; this
+module only turns torch tensors into pointers, strides and a stream, checks
+that the tensors are large enough for the pointers it passes, and raises on
+a non-zero status.  PyTorch supplies device memory and the current stream.
+There is no fallback: when the library is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libprefill_attn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "prefill_attn.h")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_WORKSPACE = 0, 1, 2, 3, 4
+PA_DTYPE_F32, PA_DTYPE_BF16, PA_DTYPE_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": PA_DTYPE_F32, "bf16": PA_DTYPE_BF16, "f16": PA_DTYPE_F16}
+PLAN_FIELDS = ("tokens_per_tile", "query_tiles", "kv_splits", "workgroups", "keys_per_tile",
+               "waves_per_workgroup", "workspace_bytes", "kv_tiles_visited")
+
+
+class PrefillAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({strerror(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(f"{LIBRARY} is missing: build it first (python -c "
+                           "'import __graft_entry__; __graft_entry__.build()')")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    tail = [I, I, I, I, I, I, P]
+    for name in ("prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, P, P, P] + tail
+        fn.restype = I
+    lib.prefill_attn_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, P, SZ, P]
+    lib.prefill_attn_ex.restype = I
+    lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.prefill_attn_workspace_bytes.restype = SZ
+    lib.prefill_attn_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I64), I]
+    lib.prefill_attn_plan.restype = I
+    lib.prefill_attn_strerror.argtypes = [I]
+    lib.prefill_attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/prefill_attn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prefill_attn\w*)\s*\(", text)))
+
+
+def strerror(status: int) -> str:
+    try:
+        return load().prefill_attn_strerror(int(status)).decode()
+    except Exception:  # the library may be what failed to load
+        return "unknown"
+
+
+def workspace_bytes(dtype: str, T, start_pos, num_heads, num_kv_heads, head_dim, window=0) -> int:
+    return int(load().prefill_attn_workspace_bytes(DTYPE_CODES[dtype], T, start_pos, num_heads,
+                                                   num_kv_heads, head_dim, window))
+
+
+def plan(dtype: str, T, start_pos, num_heads, num_kv_heads, head_dim, window=0) -> dict:
+    info = (ctypes.c_int64 * 8)()
+    st = load().prefill_attn_plan(DTYPE_CODES[dtype], T, start_pos, num_heads, num_kv_heads,
+                                  head_dim, window, info, 8)
+    if st != PA_OK:
+        raise PrefillAttnError(st, "prefill_attn_plan")
+    return dict(zip(PLAN_FIELDS, list(info)))
+
+
+# ---- torch marshalling --------------------------------------------------------
+
+def _dtype_of(t) -> str:
+    import torch
+    m = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported storage type {t.dtype}")
+    return m[t.dtype]
+
+
+def _need(t, elems: int, what: str):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous (strides are passed explicitly)")
+    if t.numel() < elems:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call reads/writes {elems}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def prefill_attn(q, k_cache, v_cache, out, T, start_pos, num_heads, num_kv_heads, head_dim,
+                 window=0, stream=None):
+    """Packed call: q [T, H*D], caches [KVH, L, D] (L = start_pos+T), out fp32 [T, H*D]."""
+    dt = _dtype_of(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one storage type")
+    import torch
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    L = start_pos + T
+    _need(q, T * num_heads * head_dim, "q")
+    _need(k_cache, num_kv_heads * L * head_dim, "k_cache")
+    _need(v_cache, num_kv_heads * L * head_dim, "v_cache")
+    _need(out, T * num_heads * head_dim, "out")
+    fn = getattr(load(), {"f32": "prefill_attn_f32", "bf16": "prefill_attn_bf16",
+                          "f16": "prefill_attn_f16"}[dt])
+    st = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), T, start_pos,
+            num_heads, num_kv_heads, head_dim, window, _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st, fn.__name__)
+    return out
+
+
+def prefill_attn_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
+                    start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
+                    stream=None):
+    """Strided call; workspace is a device tensor (any dtype) or None."""
+    dt = _dtype_of(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one storage type")
+    L = start_pos + T
+    _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
+    _need(k_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "k_cache")
+    _need(v_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "v_cache")
+    _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load().prefill_attn_ex(DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                                v_cache.data_ptr(), kv_head_stride, out.data_ptr(), out_row_stride,
+                                T, start_pos, num_heads, num_kv_heads, head_dim, window, ws_ptr,
+                                ws_bytes, _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st, "prefill_attn_ex")
+    return out

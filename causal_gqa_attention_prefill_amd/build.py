@@ -1,0 +1,34 @@
+"""Build libprefill_attn.so for gfx950 with hipcc (in-tree, no JIT cache)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = [os.path.join(HERE, "csrc", "prefill_attn.hip")]
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(HERE, "libprefill_attn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-result",
+    # packed-fp32 VALU instructions stay off: plain fp32 code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def build(output: str = LIBRARY, extra=(), verbose: bool = False) -> str:
+    tmp = output + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
+    return output
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

@@ -1,0 +1,897 @@
+// prefill_attn.hip -- fused chunked causal grouped-query prefill attention
+// for MI355X (gfx950 / CDNA4), behind the C ABI of include/prefill_attn.h.
+//
+// The computation is the one of the gnosis handoff page "Prefill attention ->
+// GPU: handoff", section "GPU design (the real fix)": scores = Q K^T scaled by
+// 1/sqrt(head_dim), causal mask (key j valid iff j <= start_pos + t), row
+// softmax, times V, with query head h reading kv head h / (H / KVH).  The
+// window band is the per-row contiguous [lo, pos] band of the TensorSharp page
+// "Design: closing the Gemma-4 long-prompt prefill gap", section 5 (Option A),
+// read as lo = pos - window + 1.
+//
+// That page's plan materialises the [heads x Tq x L] scores between two
+// strided-batched GEMMs and a softmax kernel, and its "Implementation status"
+// lists fusing the softmax into the AV step as a follow-up.  Here everything
+// is one pass over the keys (online softmax), so scores never leave
+// registers:
+//
+//   work-group  = 4 wavefronts = 128 (token, head) rows of one GQA group:
+//                 row r -> token t0 + r / G, head kvh*G + r % G, so the G
+//                 query heads that share kv head kvh share every K/V tile
+//   per KV tile of BK keys (only tiles that intersect some row's band):
+//     global -> LDS: K tile as [key][d], V tile transposed to [d][key]
+//     S^T = K Q^T   on MFMA (32x32 tiles, keys on M, rows on N); Q stays in
+//                   registers for the whole loop
+//     mask          only on tiles that cut some row's band (index compares)
+//     online softmax in fp32: each lane holds one row's scores for 16 keys
+//                   per 32-key block, so the row max needs one exchange
+//                   between the two lane halves and the row sum none
+//     O^T += V^T P^T on MFMA: the S^T accumulator registers are already in
+//                   the layout of the B operand, so P never goes through LDS;
+//                   O^T columns are rows, so the rescale by alpha is per lane
+//   epilogue    out = O / l (fp32), or per-split partials (O, m, l) that a
+//               second kernel merges when the grid is split along the keys
+//
+// bf16/fp16 inputs use v_mfma_f32_32x32x16_{bf16,f16} (P rounded to the input
+// type); fp32 inputs use v_mfma_f32_32x32x2_f32 with P kept in fp32.
+//
+// Correctness of the MFMA operand plumbing rests only on the accumulator
+// layout (lane l, register r of a 32x32 tile holds row 8*(r/4) + 4*(l/32) +
+// r%4, column l%32) and on A and B sharing the same lane/element -> k map.
+// Each contraction (over head_dim for S, over keys for O) pairs A's and B's
+// element (l/32, e) with the same index, whatever index the hardware assigns
+// to that slot.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "prefill_attn.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, work-groups dealt round-robin
+constexpr int kCus = 256;         // MI355X compute units
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Params {
+    const void *q;
+    const void *k;
+    const void *v;
+    float *out;
+    float *ws_o;      // [S][T*H][D] split partials, normalised by their own l
+    float2 *ws_ml;    // [S][T*H]    (running max of raw scores, l)
+    int64_t q_row_stride, kv_head_stride, out_row_stride;
+    int T, start_pos, H, KVH, G, window;
+    int TQ;           // query tokens per tile
+    int nq;           // query tiles
+    int S;            // key splits per tile
+    int n_items;      // nq * KVH * S work-groups
+    float c;          // log2(e) / sqrt(head_dim)
+};
+
+// ---- storage types ---------------------------------------------------------
+
+struct Bf16 {
+    __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) {
+        bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+struct F16 {
+    __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    __device__ static inline uint32_t pack(float lo, float hi) {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+};
+
+// ---- work-group -> (query tile, kv head, split) ----------------------------
+
+// Work-group b runs on die b % 8.  Give each die a contiguous range of
+// logical items so that the tiles of one kv head (and one key split) share a
+// die's L2; inside a range the query tile varies fastest.
+__device__ inline int xcd_logical_item(int b, int n) {
+    const int xcd = b % kXcds, slot = b / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    return xcd * per + min(xcd, rem) + slot;
+}
+
+__device__ inline int first_key(int pos, int window) {
+    return (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
+}
+
+struct Tile {
+    int kvh, split, t0, t_last;
+    int kt_begin, kt_end;          // this work-group's KV tiles [begin, end)
+};
+
+template <int BK>
+__device__ inline Tile locate(const Params &p) {
+    Tile w;
+    const int item = xcd_logical_item(blockIdx.x, p.n_items);
+    const int qi = item % p.nq;
+    const int rest = item / p.nq;
+    w.split = rest % p.S;
+    w.kvh = rest / p.S;
+    const int qtile = p.nq - 1 - qi;          // longest rows first
+    w.t0 = qtile * p.TQ;
+    w.t_last = min(w.t0 + p.TQ, p.T) - 1;
+    const int lo = first_key(p.start_pos + w.t0, p.window);
+    const int hi = p.start_pos + w.t_last;
+    const int kb = lo / BK, ke = hi / BK + 1;
+    const int per = (ke - kb + p.S - 1) / p.S;
+    w.kt_begin = min(ke, kb + w.split * per);
+    w.kt_end = min(ke, w.kt_begin + per);
+    return w;
+}
+
+// Per-lane row and per-wave token range.
+struct Rows {
+    int t, h, pos, lo;
+    bool ok;                       // this lane's row exists
+    bool wave_any;                 // the wave has at least one row
+    bool wave_ragged;              // the wave has lanes without a row
+    int w_pos_min, w_pos_max, w_lo_min, w_lo_max;
+};
+
+__device__ inline Rows rows_of(const Params &p, const Tile &w, int wave, int l32) {
+    Rows r;
+    const int n = wave * kRowsPerWave + l32;
+    const int tl = n / p.G;
+    r.t = w.t0 + tl;
+    r.h = w.kvh * p.G + n % p.G;
+    r.ok = tl < p.TQ && r.t <= w.t_last;
+    r.pos = r.ok ? p.start_pos + r.t : -1;
+    r.lo = r.ok ? first_key(r.pos, p.window) : 0;
+    const int tf = w.t0 + (wave * kRowsPerWave) / p.G;
+    const int tl_last = min(w.t0 + (wave * kRowsPerWave + kRowsPerWave - 1) / p.G,
+                            min(w.t0 + p.TQ - 1, w.t_last));
+    r.wave_any = (wave * kRowsPerWave) / p.G < p.TQ && tf <= w.t_last;
+    r.wave_ragged = (wave * kRowsPerWave + kRowsPerWave - 1) / p.G >= p.TQ ||
+                    w.t0 + (wave * kRowsPerWave + kRowsPerWave - 1) / p.G > w.t_last;
+    r.w_pos_min = p.start_pos + tf;
+    r.w_pos_max = p.start_pos + tl_last;
+    r.w_lo_min = first_key(r.w_pos_min, p.window);
+    r.w_lo_max = first_key(r.w_pos_max, p.window);
+    return r;
+}
+
+// ---- epilogue shared by both kernels ----------------------------------------
+
+template <int D>
+__device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r, int g,
+                                  const f32x16 (&o)[D / 32], float m, float lsum) {
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    if (!r.ok) return;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (p.S == 1) {
+        float *dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 val = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv,
+                             o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
+                *(f32x4 *)(dst + 32 * db + 8 * r4) = val;
+            }
+    } else {
+        const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
+        float *dst = p.ws_o + row * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 val = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv,
+                             o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
+                *(f32x4 *)(dst + 32 * db + 8 * r4) = val;
+            }
+        if (g == 0) p.ws_ml[row] = make_float2(m, ltot);
+    }
+}
+
+// Online-softmax step for one tile: s holds raw scores (masked ones -inf).
+// Returns alpha (the rescale of the previous accumulators) and updates m.
+template <int NB>
+__device__ inline float softmax_max(const f32x16 (&s)[NB], float &m, float c, float &mc) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mnew = fmaxf(m, mt);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
+    m = mnew;
+    mc = muse * c;
+    return alpha;
+}
+
+// ---- bf16 / fp16 kernel -------------------------------------------------------
+
+template <class Ty, int D, int BK, bool PREFETCH, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
+void attn_fwd16(Params p) {
+    static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
+    constexpr int KROW = D + 8;           // K tile row, 16 B of padding
+    constexpr int VROW = BK + 4;          // V^T tile row, 8 B of padding
+    constexpr int KVEC = BK * D / 8;      // 16-byte vectors in a K tile
+    constexpr int KPT = KVEC / kThreads;  // per thread
+    constexpr int VTASK = (BK / 2) * (D / 8);  // (key pair, 8-wide d chunk) tasks
+    constexpr int VPT = (VTASK + kThreads - 1) / kThreads;
+    static_assert(KPT * kThreads == KVEC, "staging split");
+    static_assert(VTASK % kThreads == 0 || VTASK < kThreads, "staging split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KROW];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VROW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const Tile w = locate<BK>(p);
+    const Rows r = rows_of(p, w, wave, l32);
+    const int L = p.start_pos + p.T;
+    const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride;
+    const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride;
+
+    u32x4 qreg[D / 16];
+    {
+        const uint16_t *qp = (const uint16_t *)p.q + (int64_t)(r.ok ? r.t : 0) * p.q_row_stride +
+                             (int64_t)r.h * D + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qreg[ks] = r.ok ? *(const u32x4 *)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    u32x4 kbuf[KPT];
+    u32x4 vbuf[VPT][2];
+    auto gload = [&](int kt) {
+        const int j0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * kThreads;
+            const int key = idx / (D / 8), c8 = idx % (D / 8);
+            const int j = j0 + key;
+            kbuf[i] = j < L ? *(const u32x4 *)(kbase + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * kThreads;
+            if (VTASK < kThreads && idx >= VTASK) break;
+            const int c8 = idx % (D / 8), kp = idx / (D / 8);
+            const int j = j0 + 2 * kp;
+            vbuf[i][0] = j < L ? *(const u32x4 *)(vbase + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
+            vbuf[i][1] = j + 1 < L ? *(const u32x4 *)(vbase + (int64_t)(j + 1) * D + 8 * c8)
+                                   : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * kThreads;
+            const int key = idx / (D / 8), c8 = idx % (D / 8);
+            *(u32x4 *)&Ks[key * KROW + 8 * c8] = kbuf[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * kThreads;
+            if (VTASK < kThreads && idx >= VTASK) break;
+            const int c8 = idx % (D / 8), kp = idx / (D / 8);
+            const u32x4 a = vbuf[i][0], b = vbuf[i][1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t wa = a[e / 2], wb = b[e / 2];
+                const uint32_t pair = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u))
+                                              : ((wa & 0xffffu) | (wb << 16));
+                *(uint32_t *)&Vt[(8 * c8 + e) * VROW + 2 * kp] = pair;
+            }
+        }
+    };
+
+    if (w.kt_begin < w.kt_end) {
+        if (PREFETCH) gload(w.kt_begin);
+        for (int kt = w.kt_begin; kt < w.kt_end; ++kt) {
+            if (!PREFETCH) gload(kt);
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (PREFETCH && kt + 1 < w.kt_end) gload(kt + 1);
+            const int j0 = kt * BK;
+            if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) continue;
+
+            f32x16 s[BK / 32];
+#pragma unroll
+            for (int b = 0; b < BK / 32; ++b) {
+                s[b] = f32x16{};
+                const uint16_t *kp = &Ks[(32 * b + l32) * KROW + 8 * g];
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    s[b] = Ty::mma(*(const u32x4 *)(kp + 16 * ks), qreg[ks], s[b]);
+            }
+            if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+#pragma unroll
+                for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
+                        if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                    }
+            }
+            float mc;
+            const float alpha = softmax_max<BK / 32>(s, m, p.c, mc);
+            u32x4 pb[BK / 16];
+            float ps = 0.f;
+#pragma unroll
+            for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i0 = 8 * half + 2 * jj;
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], p.c, -mc));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], p.c, -mc));
+                        ps += p0 + p1;
+                        pb[2 * b + half][jj] = Ty::pack(p0, p1);
+                    }
+            lsum = lsum * alpha + ps;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint16_t *vp = &Vt[(32 * db + l32) * VROW + 4 * g];
+#pragma unroll
+                for (int ks = 0; ks < BK / 16; ++ks) {
+                    const u32x2 lo2 = *(const u32x2 *)(vp + 16 * ks);
+                    const u32x2 hi2 = *(const u32x2 *)(vp + 16 * ks + 8);
+                    const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                    o[db] = Ty::mma(a, pb[ks], o[db]);
+                }
+            }
+        }
+    }
+    write_rows<D>(p, w, r, g, o, m, lsum);
+}
+
+// ---- fp32 kernel ---------------------------------------------------------------
+
+__device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, int BK>
+__global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
+    static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
+    constexpr int KROW = D + 4;           // floats; 16 B of padding
+    constexpr int VROW = BK + 4;
+    constexpr int KVEC = BK * D / 4;
+    constexpr int KPT = KVEC / kThreads;
+    constexpr int VTASK = (BK / 4) * (D / 4);  // (key quad, 4-wide d chunk) tasks
+    constexpr int VPT = (VTASK + kThreads - 1) / kThreads;
+    constexpr int HALF = D / 2;           // k slot (l/32) = 0 takes d < D/2, 1 the rest
+    static_assert(KPT * kThreads == KVEC, "staging split");
+    static_assert(VTASK % kThreads == 0 || VTASK < kThreads, "staging split");
+
+    __shared__ __attribute__((aligned(16))) float Ks[BK * KROW];
+    __shared__ __attribute__((aligned(16))) float Vt[D * VROW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g = lane >> 5;
+    const Tile w = locate<BK>(p);
+    const Rows r = rows_of(p, w, wave, l32);
+    const int L = p.start_pos + p.T;
+    const float *kbase = (const float *)p.k + (int64_t)w.kvh * p.kv_head_stride;
+    const float *vbase = (const float *)p.v + (int64_t)w.kvh * p.kv_head_stride;
+
+    float qreg[HALF];
+    {
+        const float *qp = (const float *)p.q + (int64_t)(r.ok ? r.t : 0) * p.q_row_stride +
+                          (int64_t)r.h * D + HALF * g;
+#pragma unroll
+        for (int i = 0; i < HALF / 4; ++i) {
+            const f32x4 v = r.ok ? *(const f32x4 *)(qp + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+            qreg[4 * i] = v[0];
+            qreg[4 * i + 1] = v[1];
+            qreg[4 * i + 2] = v[2];
+            qreg[4 * i + 3] = v[3];
+        }
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    f32x4 kbuf[KPT];
+    f32x4 vbuf[VPT][4];
+    auto gload = [&](int kt) {
+        const int j0 = kt * BK;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * kThreads;
+            const int key = idx / (D / 4), c4 = idx % (D / 4);
+            const int j = j0 + key;
+            kbuf[i] = j < L ? *(const f32x4 *)(kbase + (int64_t)j * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * kThreads;
+            if (VTASK < kThreads && idx >= VTASK) break;
+            const int c4 = idx % (D / 4), kq = idx / (D / 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + 4 * kq + u;
+                vbuf[i][u] = j < L ? *(const f32x4 *)(vbase + (int64_t)j * D + 4 * c4)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int idx = tid + i * kThreads;
+            const int key = idx / (D / 4), c4 = idx % (D / 4);
+            *(f32x4 *)&Ks[key * KROW + 4 * c4] = kbuf[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + i * kThreads;
+            if (VTASK < kThreads && idx >= VTASK) break;
+            const int c4 = idx % (D / 4), kq = idx / (D / 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f32x4 col = {vbuf[i][0][e], vbuf[i][1][e], vbuf[i][2][e], vbuf[i][3][e]};
+                *(f32x4 *)&Vt[(4 * c4 + e) * VROW + 4 * kq] = col;
+            }
+        }
+    };
+
+    if (w.kt_begin < w.kt_end) {
+        gload(w.kt_begin);
+        for (int kt = w.kt_begin; kt < w.kt_end; ++kt) {
+            __syncthreads();
+            lstore();
+            __syncthreads();
+            if (kt + 1 < w.kt_end) gload(kt + 1);
+            const int j0 = kt * BK;
+            if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) continue;
+
+            f32x16 s[BK / 32];
+#pragma unroll
+            for (int b = 0; b < BK / 32; ++b) {
+                s[b] = f32x16{};
+                const float *kp = &Ks[(32 * b + l32) * KROW + HALF * g];
+#pragma unroll
+                for (int st = 0; st < HALF; st += 4) {
+                    const f32x4 a4 = *(const f32x4 *)(kp + st);
+                    s[b] = mma_f32(a4[0], qreg[st], s[b]);
+                    s[b] = mma_f32(a4[1], qreg[st + 1], s[b]);
+                    s[b] = mma_f32(a4[2], qreg[st + 2], s[b]);
+                    s[b] = mma_f32(a4[3], qreg[st + 3], s[b]);
+                }
+            }
+            if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+#pragma unroll
+                for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
+                        if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                    }
+            }
+            float mc;
+            const float alpha = softmax_max<BK / 32>(s, m, p.c, mc);
+            float ps = 0.f;
+#pragma unroll
+            for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    s[b][i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], p.c, -mc));
+                    ps += s[b][i];
+                }
+            lsum = lsum * alpha + ps;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const float *vp = &Vt[(32 * db + l32) * VROW + 4 * g];
+#pragma unroll
+                for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4 a4 = *(const f32x4 *)(vp + 32 * b + 8 * r4);
+                        o[db] = mma_f32(a4[0], s[b][4 * r4], o[db]);
+                        o[db] = mma_f32(a4[1], s[b][4 * r4 + 1], o[db]);
+                        o[db] = mma_f32(a4[2], s[b][4 * r4 + 2], o[db]);
+                        o[db] = mma_f32(a4[3], s[b][4 * r4 + 3], o[db]);
+                    }
+            }
+        }
+    }
+    write_rows<D>(p, w, r, g, o, m, lsum);
+}
+
+// ---- split merge ------------------------------------------------------------------
+
+// out(t, h, :) = sum_s w_s O_s / sum_s w_s with w_s = l_s * 2^((m_s - m*) c),
+// m* the largest m_s among splits that saw a valid key (l_s > 0).
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const float2 *ws_ml,
+                                                    float *out, int64_t out_row_stride, int T, int H,
+                                                    int S, float c) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)T * H;
+    const int64_t row = idx / (D / 4);
+    const int d4 = (int)(idx % (D / 4));
+    if (row >= rows) return;
+    float mstar = -INFINITY;
+    for (int s = 0; s < S; ++s) {
+        const float2 ml = ws_ml[s * rows + row];
+        if (ml.y > 0.f) mstar = fmaxf(mstar, ml.x);
+    }
+    float wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+        const float2 ml = ws_ml[s * rows + row];
+        if (ml.y > 0.f) {
+            const float wgt = ml.y * __builtin_amdgcn_exp2f((ml.x - mstar) * c);
+            wsum += wgt;
+            acc += wgt * *(const f32x4 *)(ws_o + (s * rows + row) * D + 4 * d4);
+        }
+    }
+    const int t = (int)(row / H), h = (int)(row % H);
+    *(f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4) = acc * (1.f / wsum);
+}
+
+// ---- host side -----------------------------------------------------------------------
+
+using KernelFn = void (*)(Params);
+using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
+
+struct Variant {
+    int dtype, D, BK;
+    int groups_per_cu;         // resident work-groups per CU the kernel is sized for
+    KernelFn fn;
+};
+
+const Variant kVariants[] = {
+    {PA_DTYPE_BF16, 32, 64, 2, attn_fwd16<Bf16, 32, 64, true, 2>},
+    {PA_DTYPE_BF16, 64, 64, 2, attn_fwd16<Bf16, 64, 64, true, 2>},
+    {PA_DTYPE_BF16, 128, 64, 2, attn_fwd16<Bf16, 128, 64, true, 2>},
+    {PA_DTYPE_BF16, 256, 32, 1, attn_fwd16<Bf16, 256, 32, true, 1>},
+    {PA_DTYPE_BF16, 512, 32, 1, attn_fwd16<Bf16, 512, 32, false, 1>},
+    {PA_DTYPE_F16, 32, 64, 2, attn_fwd16<F16, 32, 64, true, 2>},
+    {PA_DTYPE_F16, 64, 64, 2, attn_fwd16<F16, 64, 64, true, 2>},
+    {PA_DTYPE_F16, 128, 64, 2, attn_fwd16<F16, 128, 64, true, 2>},
+    {PA_DTYPE_F16, 256, 32, 1, attn_fwd16<F16, 256, 32, true, 1>},
+    {PA_DTYPE_F16, 512, 32, 1, attn_fwd16<F16, 512, 32, false, 1>},
+    {PA_DTYPE_F32, 32, 32, 2, attn_fwd32<32, 32>},
+    {PA_DTYPE_F32, 64, 32, 2, attn_fwd32<64, 32>},
+    {PA_DTYPE_F32, 128, 32, 2, attn_fwd32<128, 32>},
+    {PA_DTYPE_F32, 256, 32, 1, attn_fwd32<256, 32>},
+};
+
+MergeFn merge_for(int D) {
+    switch (D) {
+        case 32: return merge_splits<32>;
+        case 64: return merge_splits<64>;
+        case 128: return merge_splits<128>;
+        case 256: return merge_splits<256>;
+        case 512: return merge_splits<512>;
+    }
+    return nullptr;
+}
+
+const Variant *find_variant(int dtype, int D) {
+    for (const Variant &v : kVariants)
+        if (v.dtype == dtype && v.D == D) return &v;
+    return nullptr;
+}
+
+int elem_bytes(int dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+struct Plan {
+    const Variant *var;
+    int G, TQ, nq, S, items;
+    int64_t tiles;               // KV tiles visited by all work-groups
+    size_t ws_bytes, ws_ml_offset;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int first_key_host(int64_t pos, int window) {
+    return (window > 0 && pos - window + 1 > 0) ? (int)(pos - window + 1) : 0;
+}
+
+// Shape checks shared by every entry point (no strides, no pointers).
+int check_shape(int dtype, int T, int start_pos, int H, int KVH, int D, int window) {
+    if (T < 1 || start_pos < 0 || H < 1 || KVH < 1 || D < 1 || window < 0) return PA_ERR_INVALID_ARG;
+    if (H % KVH != 0) return PA_ERR_INVALID_ARG;
+    if ((int64_t)start_pos + T > INT32_MAX) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16) return PA_ERR_UNSUPPORTED;
+    if (H / KVH > kRowsPerGroup) return PA_ERR_UNSUPPORTED;
+    if (!find_variant(dtype, D)) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Splits along the keys when the grid would leave CUs idle: pick the split
+// count whose longest-first schedule of (tile, split) items over the
+// resident work-group slots finishes first, charging each extra split the
+// cost of writing and merging its partial rows.
+int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int window,
+                  int G, int TQ, int nq) {
+    const int slots = kCus * var.groups_per_cu;
+    const int64_t base = (int64_t)nq * KVH;
+    if (base >= slots) return 1;
+    int64_t max_tiles = 0;
+    for (int q = 0; q < nq; ++q) {
+        const int t0 = q * TQ, tl = (int)std::min<int64_t>((int64_t)t0 + TQ, T) - 1;
+        const int64_t kb = first_key_host((int64_t)start_pos + t0, window) / var.BK;
+        const int64_t ke = ((int64_t)start_pos + tl) / var.BK + 1;
+        max_tiles = std::max(max_tiles, ke - kb);
+    }
+    int best = 1;
+    double best_cost = 1e300;
+    for (int S = 1; S <= 16; ++S) {
+        if (S > 1 && cdiv(max_tiles, S) < 4) break;
+        const int64_t items = base * S;
+        const double waves = (double)cdiv(items, slots);
+        // one tile's time is the unit; a split adds a partial-row write+merge
+        // of roughly half a tile for its work-group
+        const double cost = waves * (double)cdiv(max_tiles, S) + (S > 1 ? 0.5 * S : 0.0);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = S;
+        }
+    }
+    (void)H;
+    (void)G;
+    return best;
+}
+
+int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window, Plan *pl) {
+    const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
+    if (st != PA_OK) return st;
+    const Variant *var = find_variant(dtype, D);
+    pl->var = var;
+    pl->G = H / KVH;
+    pl->TQ = kRowsPerGroup / pl->G;
+    pl->nq = (int)cdiv(T, pl->TQ);
+    pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq);
+    const int64_t items = (int64_t)pl->nq * KVH * pl->S;
+    if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    pl->items = (int)items;
+    int64_t tiles = 0;
+    for (int q = 0; q < pl->nq; ++q) {
+        const int t0 = q * pl->TQ, tl = (int)std::min<int64_t>((int64_t)t0 + pl->TQ, T) - 1;
+        const int64_t kb = first_key_host((int64_t)start_pos + t0, window) / var->BK;
+        const int64_t ke = ((int64_t)start_pos + tl) / var->BK + 1;
+        tiles += ke - kb;
+    }
+    pl->tiles = tiles * KVH;
+    if (pl->S > 1) {
+        const size_t rows = (size_t)T * H;
+        const size_t o_bytes = (size_t)pl->S * rows * D * sizeof(float);
+        pl->ws_ml_offset = (o_bytes + 255) & ~(size_t)255;
+        pl->ws_bytes = pl->ws_ml_offset + (size_t)pl->S * rows * sizeof(float2);
+    } else {
+        pl->ws_ml_offset = 0;
+        pl->ws_bytes = 0;
+    }
+    return PA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const void *k,
+           const void *v, int64_t kv_head_stride, float *out, int64_t out_row_stride, int T,
+           int start_pos, int H, int KVH, int D, int window, void *ws, hipStream_t stream) {
+    Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.ws_o = pl.S > 1 ? (float *)ws : nullptr;
+    p.ws_ml = pl.S > 1 ? (float2 *)((char *)ws + pl.ws_ml_offset) : nullptr;
+    p.q_row_stride = q_row_stride;
+    p.kv_head_stride = kv_head_stride;
+    p.out_row_stride = out_row_stride;
+    p.T = T;
+    p.start_pos = start_pos;
+    p.H = H;
+    p.KVH = KVH;
+    p.G = pl.G;
+    p.window = window;
+    p.TQ = pl.TQ;
+    p.nq = pl.nq;
+    p.S = pl.S;
+    p.n_items = pl.items;
+    p.c = (float)(1.4426950408889634 / sqrt((double)D));
+    (void)dtype;
+    hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(kThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    if (pl.S > 1) {
+        const int64_t n = (int64_t)T * H * (D / 4);
+        hipLaunchKernelGGL(merge_for(D), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
+                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_row_stride, T, H,
+                           pl.S, p.c);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+}
+
+int check_args(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
+               int64_t kv_head_stride, const float *out, int64_t out_row_stride, int T,
+               int start_pos, int H, int KVH, int D, int window) {
+    if (!q || !k || !v || !out) return PA_ERR_INVALID_ARG;
+    const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
+    if (st == PA_ERR_INVALID_ARG) return st;
+    const int64_t row = (int64_t)H * D;
+    if (q_row_stride < row || out_row_stride < row) return PA_ERR_INVALID_ARG;
+    if (kv_head_stride < ((int64_t)start_pos + T) * D) return PA_ERR_INVALID_ARG;
+    if (st != PA_OK) return st;
+    const int eb = elem_bytes(dtype);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_UNSUPPORTED;
+    if ((q_row_stride * eb) % 16 || (kv_head_stride * eb) % 16 || (out_row_stride * 4) % 16)
+        return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+// Per-device scratch for the packed entry points.
+struct DeviceScratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_scratch_mutex;
+DeviceScratch g_scratch[64];
+
+int scratch_for(size_t need, void **out) {
+    *out = nullptr;
+    if (need == 0) return PA_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    DeviceScratch &s = g_scratch[dev];
+    if (s.bytes < need) {
+        if (s.ptr) {
+            // work already enqueued may still read the old buffer
+            if (hipDeviceSynchronize() != hipSuccess) return PA_ERR_HIP;
+            if (hipFree(s.ptr) != hipSuccess) return PA_ERR_HIP;
+            s.ptr = nullptr;
+            s.bytes = 0;
+        }
+        const size_t grow = need + need / 4;
+        if (hipMalloc(&s.ptr, grow) != hipSuccess) {
+            s.ptr = nullptr;
+            return PA_ERR_HIP;
+        }
+        s.bytes = grow;
+    }
+    *out = s.ptr;
+    return PA_OK;
+}
+
+int run_packed(int dtype, const void *q, const void *k, const void *v, float *out, int T,
+               int start_pos, int H, int KVH, int D, int window, void *stream) {
+    const int64_t row = (int64_t)H * D;
+    const int64_t kvs = ((int64_t)start_pos + T) * D;
+    int st = check_args(dtype, q, row, k, v, kvs, out, row, T, start_pos, H, KVH, D, window);
+    if (st != PA_OK) return st;
+    Plan pl;
+    st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
+    if (st != PA_OK) return st;
+    void *ws = nullptr;
+    st = scratch_for(pl.ws_bytes, &ws);
+    if (st != PA_OK) return st;
+    return launch(pl, dtype, q, row, k, v, kvs, out, row, T, start_pos, H, KVH, D, window, ws,
+                  (hipStream_t)stream);
+}
+
+}  // namespace
+
+// ---- C ABI -----------------------------------------------------------------------------
+
+extern "C" {
+
+int prefill_attn_f32(const float *q, const float *k_cache, const float *v_cache, float *out, int T,
+                     int start_pos, int num_heads, int num_kv_heads, int head_dim, int window,
+                     void *stream) {
+    return run_packed(PA_DTYPE_F32, q, k_cache, v_cache, out, T, start_pos, num_heads,
+                      num_kv_heads, head_dim, window, stream);
+}
+
+int prefill_attn_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                      float *out, int T, int start_pos, int num_heads, int num_kv_heads,
+                      int head_dim, int window, void *stream) {
+    return run_packed(PA_DTYPE_BF16, q, k_cache, v_cache, out, T, start_pos, num_heads,
+                      num_kv_heads, head_dim, window, stream);
+}
+
+int prefill_attn_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                     float *out, int T, int start_pos, int num_heads, int num_kv_heads,
+                     int head_dim, int window, void *stream) {
+    return run_packed(PA_DTYPE_F16, q, k_cache, v_cache, out, T, start_pos, num_heads,
+                      num_kv_heads, head_dim, window, stream);
+}
+
+int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_cache,
+                    const void *v_cache, int64_t kv_head_stride, float *out,
+                    int64_t out_row_stride, int T, int start_pos, int num_heads,
+                    int num_kv_heads, int head_dim, int window, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, out,
+                        out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window);
+    if (st != PA_OK) return st;
+    Plan pl;
+    st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl);
+    if (st != PA_OK) return st;
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
+    }
+    return launch(pl, dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, out,
+                  out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window,
+                  workspace, (hipStream_t)stream);
+}
+
+size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_heads,
+                                    int num_kv_heads, int head_dim, int window) {
+    Plan pl;
+    if (make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl) != PA_OK)
+        return 0;
+    return pl.ws_bytes;
+}
+
+int prefill_attn_plan(int dtype, int T, int start_pos, int num_heads, int num_kv_heads,
+                      int head_dim, int window, int64_t *info, int n) {
+    Plan pl;
+    const int st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl);
+    if (st != PA_OK) return st;
+    const int64_t vals[8] = {pl.TQ, pl.nq, pl.S, pl.items, pl.var->BK, kWaves,
+                             (int64_t)pl.ws_bytes, pl.tiles};
+    for (int i = 0; i < n && i < 8 && info; ++i) info[i] = vals[i];
+    return PA_OK;
+}
+
+const char *prefill_attn_strerror(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, group size or alignment";
+        case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

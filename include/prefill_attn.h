@@ -1,0 +1,141 @@
+/*
+ * prefill_attn.h -- C ABI of the MI355X (gfx950) chunked causal grouped-query
+ * prefill attention library, libprefill_attn.so.
+ *
+ * The operation (gnosis handoff page "Prefill attention -> GPU: handoff",
+ * section "GPU design (the real fix)"):
+ *
+ *   A chunk of T query tokens at absolute positions start_pos .. start_pos+T-1
+ *   attends to the L = start_pos + T keys held in a KV cache.  Query head h
+ *   reads kv head h / (num_heads / num_kv_heads) (grouped-query attention).
+ *   For query token t (position pos = start_pos + t) and each valid key j:
+ *       s_j = (q_t . k_j) / sqrt(head_dim)
+ *   valid keys are j <= pos (causal mask, Step 2 of that section) and, when
+ *   window > 0, j >= pos - window + 1 (the per-row contiguous band of the
+ *   TensorSharp page "Design: closing the Gemma-4 long-prompt prefill gap",
+ *   section 5, Option A: `window` keys including the query's own).  The row
+ *   softmax of the valid scores weights the value rows:
+ *       out_t = sum_j softmax(s)_j * v_j                      (Step 3)
+ *   Masked keys contribute exactly nothing.  window <= 0 means no window.
+ *
+ * Layouts (all element offsets, row-major; same page, "Layout"):
+ *   q        (t, h, d)  at q[t*q_row_stride + h*head_dim + d]
+ *            packed entry points: q_row_stride = num_heads*head_dim (the
+ *            page's qkv_dim)
+ *   k_cache, v_cache
+ *            (kh, j, d) at k_cache[kh*kv_head_stride + j*head_dim + d],
+ *            one contiguous [L x head_dim] block per kv head; packed entry
+ *            points: kv_head_stride = L*head_dim.  A cache allocated for
+ *            `capacity` positions passes kv_head_stride = capacity*head_dim
+ *            to prefill_attn_ex; rows L .. capacity-1 are never read, so
+ *            they may hold anything, NaN included.
+ *   out      (t, h, d)  at out[t*out_row_stride + h*head_dim + d], fp32;
+ *            packed entry points: out_row_stride = num_heads*head_dim.
+ *
+ * Storage types: fp32, bf16 or fp16 for q/k/v (bf16 and fp16 passed as
+ * uint16_t bit patterns), fp32 for out.  bf16/fp16 inputs are multiplied on
+ * the matrix cores with fp32 accumulation; the softmax runs in fp32.
+ *
+ * Supported shapes: head_dim in {32, 64, 128, 256, 512} for bf16/fp16 and
+ * {32, 64, 128, 256} for fp32; any T >= 1, start_pos >= 0, num_heads a
+ * multiple of num_kv_heads with num_heads/num_kv_heads <= 128.  Pointers must
+ * be 16-byte aligned and q_row_stride, kv_head_stride and out_row_stride
+ * must keep every row 16-byte aligned.
+ *
+ * Ownership: every pointer is caller-owned device memory.  The library keeps
+ * no pointer after a call returns, never frees caller memory, only reads q,
+ * k_cache and v_cache, and writes every element (t, h, d) of out (nothing
+ * else in out's rows).
+ *
+ * Errors: arguments are checked before anything is enqueued; a violation
+ * returns PA_ERR_INVALID_ARG (or PA_ERR_UNSUPPORTED for a shape or alignment
+ * the library has no kernel for) and leaves out untouched.  A failed launch
+ * returns PA_ERR_HIP.  Calls are asynchronous on `stream` (a hipStream_t,
+ * NULL for the null stream): faults inside a kernel surface at the caller's
+ * next synchronisation, as usual for HIP.  No C++ exception crosses this
+ * interface.
+ */
+#ifndef PREFILL_ATTN_H
+#define PREFILL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG 1   /* null pointer, T < 1, start_pos < 0, heads < 1,
+                                  num_heads % num_kv_heads != 0, window < 0,
+                                  a stride below its minimum                      */
+#define PA_ERR_UNSUPPORTED 2   /* head_dim, dtype, group size or alignment       */
+#define PA_ERR_HIP 3           /* a HIP runtime call or launch failed             */
+#define PA_ERR_WORKSPACE 4     /* workspace missing or smaller than required      */
+
+/* storage types of q, k_cache and v_cache */
+#define PA_DTYPE_F32 0
+#define PA_DTYPE_BF16 1
+#define PA_DTYPE_F16 2
+
+/*
+ * Packed entry points: q [T][num_heads][head_dim], caches
+ * [num_kv_heads][L][head_dim] with L = start_pos + T, out [T][num_heads][head_dim].
+ * When the launch needs scratch memory for split-KV partial results the
+ * library takes it from a per-device buffer it allocates on first need and
+ * grows (hipMalloc; growing synchronises the device once).  Calls that run
+ * concurrently on one device share that buffer and must be ordered on one
+ * stream.
+ */
+int prefill_attn_f32(const float *q, const float *k_cache, const float *v_cache, float *out,
+                     int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                     int window, void *stream);
+int prefill_attn_bf16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                      float *out, int T, int start_pos, int num_heads, int num_kv_heads,
+                      int head_dim, int window, void *stream);
+int prefill_attn_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                     float *out, int T, int start_pos, int num_heads, int num_kv_heads,
+                     int head_dim, int window, void *stream);
+
+/*
+ * General form: explicit strides (in elements) and an explicit workspace.
+ * dtype is a PA_DTYPE_* value.  workspace may be NULL when
+ * prefill_attn_workspace_bytes() returns 0 for the same arguments; otherwise
+ * it must be device memory of at least that many bytes, 256-byte aligned,
+ * and it must not be used by anything else until the work enqueued by this
+ * call has finished.  Nothing is allocated.
+ */
+int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride,
+                    const void *k_cache, const void *v_cache, int64_t kv_head_stride,
+                    float *out, int64_t out_row_stride,
+                    int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                    int window, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Scratch bytes prefill_attn_ex needs for these arguments (0: none).
+ * Returns 0 as well for arguments that are invalid or unsupported.
+ */
+size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_heads,
+                                    int num_kv_heads, int head_dim, int window);
+
+/*
+ * Launch plan for these arguments, for tests and tuning: fills up to n
+ * entries of info with
+ *   [0] query tokens per work-group tile     [1] query tiles
+ *   [2] KV splits per tile (1: no split)     [3] work-groups launched
+ *   [4] keys per KV tile                     [5] wavefronts per work-group
+ *   [6] workspace bytes                      [7] KV tiles visited in total
+ * and returns PA_OK or the status the same call would return.
+ */
+int prefill_attn_plan(int dtype, int T, int start_pos, int num_heads, int num_kv_heads,
+                      int head_dim, int window, int64_t *info, int n);
+
+/* Static text for a status code. */
+const char *prefill_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFILL_ATTN_H */

@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments before anything is enqueued."""
+import ctypes
+
+import pytest
+
+import causal_gqa_attention_prefill_amd as pa
+from causal_gqa_attention_prefill_amd import binding
+
+FAKE = 0x10000  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = pa.header_functions()
+    assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
+                          "prefill_attn_ex", "prefill_attn_workspace_bytes", "prefill_attn_plan",
+                          "prefill_attn_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror(lib):
+    for code in range(5):
+        assert pa.strerror(code) not in ("", "unknown status")
+    assert pa.strerror(99) == "unknown status"
+
+
+def _packed(lib, fn, q=FAKE, k=FAKE, v=FAKE, out=FAKE, T=4, sp=0, H=4, KVH=2, D=64, W=0):
+    return getattr(lib, fn)(q, k, v, out, T, sp, H, KVH, D, W, None)
+
+
+@pytest.mark.parametrize("fn", ["prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16"])
+def test_invalid_arguments(lib, fn):
+    E = pa.PA_ERR_INVALID_ARG
+    assert _packed(lib, fn, q=None) == E
+    assert _packed(lib, fn, k=None) == E
+    assert _packed(lib, fn, v=None) == E
+    assert _packed(lib, fn, out=None) == E
+    assert _packed(lib, fn, T=0) == E
+    assert _packed(lib, fn, T=-3) == E
+    assert _packed(lib, fn, sp=-1) == E
+    assert _packed(lib, fn, H=0) == E
+    assert _packed(lib, fn, KVH=0) == E
+    assert _packed(lib, fn, H=6, KVH=4) == E
+    assert _packed(lib, fn, W=-1) == E
+    assert _packed(lib, fn, T=2**30, sp=2**30 + 5) == E
+
+
+@pytest.mark.parametrize("fn", ["prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16"])
+def test_unsupported(lib, fn):
+    U = pa.PA_ERR_UNSUPPORTED
+    for D in (16, 48, 100, 1024):
+        assert _packed(lib, fn, D=D) == U
+    assert _packed(lib, fn, H=256, KVH=1) == U       # group larger than a work-group's rows
+    assert _packed(lib, fn, q=FAKE + 4) == U          # misaligned
+    if fn == "prefill_attn_f32":
+        assert _packed(lib, fn, D=512) == U
+
+
+def test_ex_strides_and_workspace(lib):
+    ex = lib.prefill_attn_ex
+    # strides below their minimum
+    assert ex(1, FAKE, 100, FAKE, FAKE, 64 * 10, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 9, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 10, FAKE, 127, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    # unknown dtype
+    assert ex(7, FAKE, 128, FAKE, FAKE, 640, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    # a row stride that breaks 16-byte alignment of rows
+    assert ex(1, FAKE, 132, FAKE, FAKE, 640, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    # a split plan without (or with too little) workspace
+    need = pa.workspace_bytes("bf16", 64, 8000, 8, 8, 128)
+    assert need > 0
+    args = (1, FAKE, 8 * 128, FAKE, FAKE, 8064 * 128, FAKE, 8 * 128, 64, 8000, 8, 8, 128, 0)
+    assert ex(*args, None, 0, None) == pa.PA_ERR_WORKSPACE
+    assert ex(*args, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
+    assert ex(*args, FAKE + 16, need, None) == pa.PA_ERR_WORKSPACE   # not 256-byte aligned
+
+
+def test_plan_shapes():
+    p = pa.plan("bf16", 2048, 6144, 32, 8, 128)
+    assert p["tokens_per_tile"] * 4 == 128 and p["query_tiles"] == 64
+    assert p["workgroups"] == 64 * 8 * p["kv_splits"]
+    assert p["waves_per_workgroup"] == 4
+    # every (tile, kv head) visits only KV tiles that hold a valid key of one of its rows
+    bk = p["keys_per_tile"]
+    tiles = 0
+    for qt in range(64):
+        lo_pos, hi_pos = 6144 + 32 * qt, 6144 + 32 * qt + 31
+        tiles += hi_pos // bk - 0 // bk + 1
+    assert p["kv_tiles_visited"] == tiles * 8
+    # the window keeps a tile's KV range to ~window + tile keys
+    w = pa.plan("bf16", 2048, 129024, 8, 4, 256, 1024)
+    per_tile = w["kv_tiles_visited"] / (w["query_tiles"] * 4)
+    assert per_tile <= (1024 + w["tokens_per_tile"]) / w["keys_per_tile"] + 2
+    assert pa.workspace_bytes("bf16", 2048, 6144, 32, 8, 128) == p["workspace_bytes"]
+    with pytest.raises(pa.PrefillAttnError):
+        pa.plan("bf16", 4, 0, 6, 4, 64)
+
+
+def test_binding_has_no_cpu_path():
+    src = open(binding.__file__).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    assert "numpy" not in src

@@ -1,0 +1,243 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI.
+
+Full comparisons at sizes the oracle finishes in seconds (many tiles and a
+ragged tail), and sampled rows at the five workloads' full sizes in the
+launch configuration the benchmark times.  Bars: max |gpu - oracle| <= 1e-4
+for fp32 inputs, <= 2e-2 for bf16/fp16 (fp32 output), plus a relative-RMS
+bar (gpu_util.TOL_REL_RMS)."""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_util import assert_parity, device, run_packed, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    assert torch.cuda.is_available(), "no GPU"
+    pa.load()
+
+
+# ---- full comparisons on small shapes ---------------------------------------
+
+SMALL = []
+for dtype, D in [("f32", 32), ("f32", 64), ("f32", 128), ("f32", 256),
+                 ("bf16", 32), ("bf16", 64), ("bf16", 128), ("bf16", 256), ("bf16", 512),
+                 ("f16", 64), ("f16", 128), ("f16", 256), ("f16", 512)]:
+    for (H, KVH), (T, sp), W in [((4, 2), (77, 0), 0), ((8, 2), (130, 300), 0), ((8, 8), (5, 37), 0),
+                                 ((8, 1), (200, 41), 50), ((6, 3), (33, 100), 1), ((4, 4), (1, 0), 0)]:
+        SMALL.append((dtype, D, H, KVH, T, sp, W))
+
+
+@pytest.mark.parametrize("dtype,D,H,KVH,T,sp,W", SMALL,
+                         ids=[f"{c[0]}-D{c[1]}-H{c[2]}/{c[3]}-T{c[4]}-sp{c[5]}-W{c[6]}" for c in SMALL])
+def test_small_full(orc, dtype, D, H, KVH, T, sp, W):
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=T * 7 + sp + D + W, dtype=dtype)
+    got = run_packed(x, T, sp, H, KVH, D, W)
+    ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W)
+    assert_parity(got, ref, dtype, f"{dtype} D{D} {H}/{KVH} T{T} sp{sp} W{W}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_peaked_softmax(orc, dtype):
+    """Q scaled up 16x: peaked rows, large running-max jumps and rescales."""
+    H, KVH, D, T, sp = 8, 2, 128, 150, 420
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=11, dtype=dtype)
+    q16 = x.q_f32 * np.float32(16.0)
+    if dtype == "bf16":
+        q_store = workloads.round_to_bf16_bits(q16)
+        q16 = workloads.bf16_bits_to_f32(q_store)
+    else:
+        q_store = q16
+    got = run_packed(x, T, sp, H, KVH, D, 0, q_rows=q_store)
+    ref = orc.attention(q16, x.k_f32, x.v_f32, T, sp, H, KVH, D)
+    assert_parity(got, ref, dtype, f"{dtype} Qx16")
+
+
+def test_planted_keys_outside_band(orc):
+    """Keys right past the causal bound and right before the window start get
+    huge scores; none may leak into any row."""
+    H, KVH, D, T, sp, W = 4, 2, 128, 64, 200, 40
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=5, dtype="f32")
+    k = x.k_f32.copy()
+    v = x.v_f32.copy()
+    qh = x.q_f32.reshape(T, H, D)
+    for t in (0, 17, 40):
+        pos = sp + t
+        for j in (pos + 1, pos - W):
+            for kh in range(KVH):
+                k[kh, j] = 20.0 * np.sign(qh[t, kh * (H // KVH)])
+                v[kh, j] = 100.0
+    x.k_store, x.v_store, x.k_f32, x.v_f32 = k, v, k, v
+    got = run_packed(x, T, sp, H, KVH, D, W)
+    ref = orc.attention(x.q_f32, k, v, T, sp, H, KVH, D, window=W)
+    assert_parity(got, ref, "f32", "planted keys")
+
+
+def test_closed_form_band_f32():
+    """q = 0: every valid key equally likely; V[kh, j, :] = j + 1000*kh gives
+    out = (lo + pos)/2 + 1000*kv_head(h) exactly up to fp32 rounding."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    for H, KVH, D, T, sp, W in ((8, 2, 64, 100, 0, 0), (8, 2, 64, 100, 900, 0), (8, 4, 128, 70, 500, 33),
+                                (4, 1, 32, 40, 10, 1)):
+        L = sp + T
+        q = torch.zeros(T, H * D, device=device())
+        k = torch.randn(KVH, L, D, device=device())
+        v = (torch.arange(L, device=device(), dtype=torch.float32)[None, :, None]
+             + 1000.0 * torch.arange(KVH, device=device(), dtype=torch.float32)[:, None, None]).expand(KVH, L, D).contiguous()
+        out = torch.empty(T, H * D, device=device())
+        pa.prefill_attn(q, k, v, out, T, sp, H, KVH, D, W)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().reshape(T, H, D)
+        pos = sp + np.arange(T)
+        lo = np.maximum(0, pos - W + 1) if W > 0 else np.zeros_like(pos)
+        want = (lo + pos)[:, None, None] / 2.0 + 1000.0 * (np.arange(H) // (H // KVH))[None, :, None]
+        err = np.abs(o - want).max()
+        assert err <= 1e-6 * max(1.0, float(np.abs(want).max())), (H, KVH, D, T, sp, W, err)
+
+
+# ---- strided form, capacity caches, non-finite tails, untouched padding --------
+
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("bf16", 128), ("bf16", 512), ("f16", 256)])
+def test_ex_strided_nan_tail(orc, dtype, D):
+    """Q inside a fused QKV row (stride (H + 2 KVH) D), a cache allocated for
+    more positions than L whose tail is NaN, and an output with padded rows:
+    the NaN tail must never be read and the padding never written."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    H, KVH, T, sp, W = 8, 2, 90, 150, 0
+    L, cap = sp + T, sp + T + 77
+    x = workloads.make_random(H, KVH, D, T, sp, capacity=cap, std=0.5, seed=3, dtype=dtype)
+    qs = (H + 2 * KVH) * D
+    q_fused = np.zeros((T, qs), dtype=x.q_store.dtype)
+    q_fused[:, :H * D] = x.q_store
+    k_store, v_store = x.k_store.copy(), x.v_store.copy()
+    nan_bits = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00)}[dtype]
+    k_store[:, L:] = nan_bits
+    v_store[:, L:] = nan_bits
+    q = to_device(q_fused, dtype)
+    k = to_device(k_store, dtype)
+    v = to_device(v_store, dtype)
+    ors = H * D + 16
+    out = torch.full((T, ors), float("nan"), device=device())
+    ws_bytes = pa.workspace_bytes(dtype, T, sp, H, KVH, D, W)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device()) if ws_bytes else None
+    pa.prefill_attn_ex(q, qs, k, v, cap * D, out, ors, T, sp, H, KVH, D, W, workspace=ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isnan(o[:, H * D:]).all(), "padding written"
+    got = o[:, :H * D].reshape(T, H, D)
+    ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W, kv_head_stride=cap * D)
+    assert_parity(got, ref, dtype, f"ex {dtype} D{D}")
+
+
+def test_split_path(orc):
+    """Few query tiles over a long cache: the plan splits the keys and merges."""
+    import causal_gqa_attention_prefill_amd as pa
+    for dtype, H, KVH, D, T, sp, W in (("bf16", 8, 8, 128, 64, 6000, 0), ("f32", 4, 4, 64, 40, 3000, 0),
+                                       ("bf16", 8, 2, 256, 100, 5000, 700), ("f16", 4, 1, 512, 20, 4000, 0)):
+        assert pa.plan(dtype, T, sp, H, KVH, D, W)["kv_splits"] > 1
+        x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=sp, dtype=dtype)
+        got = run_packed(x, T, sp, H, KVH, D, W)
+        ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W)
+        assert_parity(got, ref, dtype, f"split {dtype} D{D}")
+
+
+def test_chunked_matches_one_shot(orc):
+    """A prompt prefilled in chunks through a growing cache equals the rows of
+    the one-shot prefill (both against the oracle), and T = 1 decode steps too."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    H, KVH, D, N = 8, 2, 128, 700
+    x = workloads.make_random(H, KVH, D, N, 0, std=0.5, seed=21, dtype="bf16")
+    ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, N, 0, H, KVH, D)
+    k = to_device(x.k_store, "bf16")
+    v = to_device(x.v_store, "bf16")
+    start = 0
+    for T in (256, 1, 200, 243):
+        q = to_device(x.q_store[start:start + T], "bf16")
+        out = torch.empty(T, H * D, device=device())
+        ws_b = pa.workspace_bytes("bf16", T, start, H, KVH, D, 0)
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=device()) if ws_b else None
+        pa.prefill_attn_ex(q, H * D, k, v, N * D, out, H * D, T, start, H, KVH, D, 0, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out.cpu().numpy().reshape(T, H, D), ref[start:start + T], "bf16", f"chunk at {start}")
+        start += T
+
+
+def test_deterministic(orc):
+    """The same call twice gives the same bits."""
+    H, KVH, D, T, sp = 32, 8, 128, 300, 1000
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=9, dtype="bf16")
+    a = run_packed(x, T, sp, H, KVH, D, 0)
+    b = run_packed(x, T, sp, H, KVH, D, 0)
+    assert np.array_equal(a, b)
+
+
+# ---- the five workloads at full size ----------------------------------------------
+
+def _sample_rows(T, H, n_random, seed):
+    rng = np.random.default_rng(seed)
+    ts = sorted({0, 1, 31, 32, 63, 64, T // 2, T - 33, T - 2, T - 1} & set(range(T)))
+    rows = [(t, h) for t in ts for h in (0, H // 2, H - 1)]
+    rows += [(int(a), int(b)) for a, b in zip(rng.integers(0, T, n_random), rng.integers(0, H, n_random))]
+    return np.array([r[0] for r in rows]), np.array([r[1] for r in rows])
+
+
+def _run_workload(orc, name, n_random=64):
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl)
+    H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
+    k = to_device(x.k_store, wl.dtype)
+    v = to_device(x.v_store, wl.dtype)
+    for ci, (T, sp) in enumerate(wl.chunks):
+        q_store, q_f32 = x.q_rows(ci)
+        q = to_device(q_store, wl.dtype)
+        out = torch.empty(T, H * D, device=device())
+        ws_b = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=device()) if ws_b else None
+        pa.prefill_attn_ex(q, H * D, k, v, wl.capacity * D, out, H * D, T, sp, H, KVH, D, W, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().reshape(T, H, D)
+        if T * H <= 64 * 1024 and (sp + T) * T * H * D <= 2e10:
+            ref = orc.attention(q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W,
+                                kv_head_stride=wl.capacity * D)
+            assert_parity(got, ref, wl.dtype, f"{name} chunk {ci} (all rows)")
+        else:
+            rt, rh = _sample_rows(T, H, n_random, seed=wl.seed + ci)
+            ref = orc.rows(q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh, window=W,
+                           kv_head_stride=wl.capacity * D)
+            assert_parity(got[rt, rh], ref, wl.dtype, f"{name} chunk {ci} ({len(rt)} sampled rows)")
+        # every row is finite and every row's output is a convex combination
+        assert np.isfinite(got).all()
+
+
+def test_workload_tiny_f32(orc):
+    _run_workload(orc, "tiny_f32")
+
+
+def test_workload_mistral_f32(orc):
+    _run_workload(orc, "mistral_f32")
+
+
+def test_workload_mistral_bf16_chunked(orc):
+    _run_workload(orc, "mistral_bf16_chunked")
+
+
+def test_workload_gemma_global_bf16(orc):
+    _run_workload(orc, "gemma_global_bf16", n_random=32)
+
+
+def test_workload_gemma_swa_bf16(orc):
+    _run_workload(orc, "gemma_swa_bf16")
