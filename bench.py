@@ -1,0 +1,227 @@
+"""Benchmark of chunked causal GQA prefill attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the Mistral-7B-shaped bf16 prefill of an 8192-token prompt as four T=2048
+chunks (start_pos 0, 2048, 4096, 6144) into a cache allocated for 8192
+positions (32 query / 8 kv heads, head_dim 128), i.e. four calls of the C
+ABI.  Inputs are resident in HBM before the timed region starts.
+
+Output: one JSON line.  ``value`` is attention TFLOP/s over the timed steps,
+FLOPs = 4 * heads * head_dim * (valid (query, key) pairs) per call.  The
+``roofline`` object prices the fused kernel against the dense bf16 MFMA peak
+(HIP events around each launch on the stream it runs on); ``cpu_baseline``
+times the fp64 oracle on a bounded sample of the same workload on the host
+cores.  Diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "prefill attention TFLOP/s and % of MI355X bf16 MFMA peak (T=2048 chunk)"
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
+HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "causal_gqa_attention_prefill_amd", "csrc", "prefill_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def valid_pairs(T: int, start_pos: int, window: int) -> int:
+    """Valid (query, key) pairs of one chunk: row t keeps keys lo..pos."""
+    pos = np.arange(start_pos, start_pos + T, dtype=np.int64)
+    lo = np.maximum(0, pos - window + 1) if window > 0 else np.zeros_like(pos)
+    return int((pos - lo + 1).sum())
+
+
+def attention_flops(T: int, start_pos: int, num_heads: int, head_dim: int, window: int) -> int:
+    """One multiply-add (2 flops) per element for q.k and again for p.v."""
+    return 4 * num_heads * head_dim * valid_pairs(T, start_pos, window)
+
+
+def algorithmic_bytes(wl, T: int, start_pos: int) -> int:
+    """Each input element read once, each output element written once: Q rows
+    of the chunk, K and V rows the chunk's bands touch, fp32 output."""
+    eb = 4 if wl.dtype == "f32" else 2
+    lo_first = max(0, start_pos - wl.window + 1) if wl.window > 0 else 0
+    keys = start_pos + T - lo_first
+    return (T * wl.num_heads * wl.head_dim * eb + 2 * wl.num_kv_heads * keys * wl.head_dim * eb
+            + T * wl.num_heads * wl.head_dim * 4)
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters, kept
+    with the digest of the kernel source they were taken on; None once the
+    source has changed."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, x, target_s: float):
+    """The fp64 oracle on the host cores, on sampled rows of the same chunks."""
+    import oracle
+    orc = oracle.default()
+    threads = oracle.default_threads()
+    H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
+    rng = np.random.default_rng(12345)
+
+    def run(rows_per_chunk):
+        flops, t_total, n = 0, 0.0, 0
+        for ci, (T, sp) in enumerate(wl.chunks):
+            _, q_f32 = x.q_rows(ci)
+            rt = rng.integers(0, T, rows_per_chunk)
+            rh = rng.integers(0, H, rows_per_chunk)
+            t0 = time.perf_counter()
+            orc.rows(q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh, window=W,
+                     kv_head_stride=wl.capacity * D, nthreads=threads)
+            t_total += time.perf_counter() - t0
+            pos = sp + rt
+            lo = np.maximum(0, pos - W + 1) if W > 0 else np.zeros_like(pos)
+            flops += int(4 * D * (pos - lo + 1).sum())
+            n += rows_per_chunk
+        return flops, t_total, n
+
+    f, t, _ = run(threads * 4)                       # pilot
+    rate = f / max(t, 1e-9)
+    per_row = f / (threads * 4 * len(wl.chunks))
+    rows = max(threads, int(target_s * rate / per_row / len(wl.chunks)))
+    f, t, n = run(rows)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} (token, head) rows drawn uniformly from the {len(wl.chunks)} chunks "
+                      f"({rows} per chunk), fp64 oracle, {t:.1f} s wall, {f / 1e9:.1f} GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(each GPU would run its own shard of kv heads; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    pa.load()
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[args.workload]
+    H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
+
+    t0 = time.perf_counter()
+    x = workloads.make_inputs(wl)
+
+    def dev_tensor(a):
+        if wl.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return t.view(torch.bfloat16 if wl.dtype == "bf16" else torch.float16)
+
+    k = dev_tensor(x.k_store)
+    v = dev_tensor(x.v_store)
+    calls = []
+    for ci, (T, sp) in enumerate(wl.chunks):
+        q = dev_tensor(x.q_rows(ci)[0])
+        out = torch.empty(T, H * D, dtype=torch.float32, device=dev)
+        nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        calls.append((q, out, ws, T, sp))
+    torch.cuda.synchronize()
+    print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    flops_step = sum(attention_flops(T, sp, H, D, W) for T, sp in wl.chunks)
+    bytes_step = sum(algorithmic_bytes(wl, T, sp) for T, sp in wl.chunks)
+
+    def step(events=None):
+        for i, (q, out, ws, T, sp) in enumerate(calls):
+            if events is not None:
+                events[i][0].record()
+            pa.prefill_attn_ex(q, H * D, k, v, wl.capacity * D, out, H * D, T, sp, H, KVH, D, W,
+                               workspace=ws)
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    launch_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])  # [steps, calls]
+    per_call_ms = launch_ms.mean(axis=0)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = flops_step / (elapsed / args.steps) / 1e12
+    # the fused kernel (with the merge kernel when a call splits its keys):
+    # algorithmic flops per launch over its average launch duration
+    achieved = flops_step / len(calls) / (per_call_ms.mean() * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    traffic = read_traffic(wl.name)
+    for i, (T, sp) in enumerate(wl.chunks):
+        f = attention_flops(T, sp, H, D, W)
+        b = algorithmic_bytes(wl, T, sp)
+        print(f"call {i}: T={T} start_pos={sp} {per_call_ms[i] * 1e3:8.1f} us  "
+              f"{f / per_call_ms[i] / 1e9:7.1f} TFLOP/s  {100 * f / per_call_ms[i] / 1e9 / peak:5.1f}% of peak  "
+              f"{b / per_call_ms[i] / 1e6:7.1f} GB/s algorithmic  plan={pa.plan(wl.dtype, T, sp, H, KVH, D, W)}",
+              file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.summary, "num_heads": H,
+                   "num_kv_heads": KVH, "head_dim": D, "window": W,
+                   "chunks": [list(c) for c in wl.chunks], "cache_capacity": wl.capacity,
+                   "flops_per_step": flops_step, "algorithmic_bytes_per_step": bytes_step,
+                   "peak_fraction": round(value / peak, 4), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
