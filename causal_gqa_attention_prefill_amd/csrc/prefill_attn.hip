@@ -86,6 +86,7 @@ struct Params {
     int S;            // key splits per tile
     int n_items;      // nq * KVH * S work-groups
     float c;          // log2(e) / sqrt(head_dim)
+    int kv_bytes;     // bytes of the L valid rows of one kv head (16-bit kernels)
 };
 
 // ---- storage types ---------------------------------------------------------
@@ -185,10 +186,14 @@ __device__ inline Rows rows_of(const Params &p, const Tile &w, int wave, int l32
 
 // ---- epilogue shared by both kernels ----------------------------------------
 
+// Value of lane l combined with lane l ^ 32 (the other half of the wave).
+__device__ inline float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ inline float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+
 template <int D>
 __device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r, int g,
-                                  const f32x16 (&o)[D / 32], float m, float lsum) {
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+                                  const f32x16 (&o)[D / 32], float mc, float lsum) {
+    const float ltot = sum_halves(lsum);
     if (!r.ok) return;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (p.S == 1) {
@@ -212,7 +217,7 @@ __device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r,
                              o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
                 *(f32x4 *)(dst + 32 * db + 8 * r4) = val;
             }
-        if (g == 0) p.ws_ml[row] = make_float2(m, ltot);
+        if (g == 0) p.ws_ml[row] = make_float2(mc, ltot);
     }
 }
 
@@ -225,7 +230,7 @@ __device__ inline float softmax_max(const f32x16 (&s)[NB], float &m, float c, fl
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[b][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_halves(mt);
     const float mnew = fmaxf(m, mt);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
@@ -235,30 +240,109 @@ __device__ inline float softmax_max(const f32x16 (&s)[NB], float &m, float c, fl
 }
 
 // ---- bf16 / fp16 kernel -------------------------------------------------------
+//
+// K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+// destination, no register staging), double-buffered so that the loads of
+// tile i+1 run under the math of tile i, with one barrier per tile.  The
+// buffer descriptor of each kv head is limited to its L rows, so rows past
+// L read as zero and are never fetched.  Both tiles are stored row-major
+// ([key][d], 16-byte chunks) with an XOR swizzle of the chunk index instead
+// of padding:
+//   K: chunk c of row r sits at c ^ swz_k(r): the 16 rows one ds_read_b128
+//      phase touches land in 16 different bank groups;
+//   V: chunk c of row r sits at c ^ swz_v(r): the 4 rows x 4 chunks one
+//      transposed read touches per half-wave land in 16 different groups.
+// V^T operands come from ds_read_b64_tr_b16: inside each 16-lane group,
+// output lane 4q+e gets element e of the rows addressed by lanes q, q+4,
+// q+8, q+12, so lanes that address rows (key0 + 4*(l/32) + j/4) at column
+// (d0 + 16*((l/16)%2) + 4*(j%4)), j = l%16, receive
+// V[key0 + 4*(l/32) + r][d0 + l%32], r = 0..3: the A operand of V^T P^T.
 
-template <class Ty, int D, int BK, bool PREFETCH, int WAVES_PER_SIMD>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+#define LDS_I16X4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
+
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer descriptors exist in the device pass only
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bytes) {
+    // raw buffer, stride 0, range `bytes` (gfx9 data-format word)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+#endif
+
+[[maybe_unused]] __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+template <int CPR>
+__device__ inline int swz_k(int row) {
+    if constexpr (CPR >= 16) return row & 15;
+    else if constexpr (CPR == 8) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
+}
+
+template <int CPR>
+__device__ inline int swz_v(int row) {
+    if constexpr (CPR >= 16) return 4 * (row & 3);
+    else if constexpr (CPR == 8) return 4 * ((row >> 1) & 1);
+    else return 0;
+}
+
+struct Ones {
+    __device__ static inline float dot(uint32_t p2, float acc, Bf16) {
+        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p2), one, acc, false);
+    }
+    __device__ static inline float dot(uint32_t p2, float acc, F16) {
+        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p2), one, acc, false);
+    }
+};
+
+[[maybe_unused]] constexpr float kRescaleLog2 = 8.f;   // keep a stale row max while p <= 2^8
+
+template <class Ty, int D, int BK, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
+#if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
-    constexpr int KROW = D + 8;           // K tile row, 16 B of padding
-    constexpr int VROW = BK + 4;          // V^T tile row, 8 B of padding
-    constexpr int KVEC = BK * D / 8;      // 16-byte vectors in a K tile
-    constexpr int KPT = KVEC / kThreads;  // per thread
-    constexpr int VTASK = (BK / 2) * (D / 8);  // (key pair, 8-wide d chunk) tasks
-    constexpr int VPT = (VTASK + kThreads - 1) / kThreads;
-    static_assert(KPT * kThreads == KVEC, "staging split");
-    static_assert(VTASK % kThreads == 0 || VTASK < kThreads, "staging split");
+    constexpr int CPR = D / 8;                        // 16-byte chunks per row
+    constexpr int TILE_CHUNKS = BK * CPR;
+    constexpr int TILE_BYTES = TILE_CHUNKS * 16;
+    constexpr int LOADS = TILE_CHUNKS / (kWaves * kWave);   // per wave, per matrix, per tile
+    static_assert(LOADS * kWaves * kWave == TILE_CHUNKS, "staging split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VROW];
+    // [buffer][K, V][TILE_BYTES]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE_BYTES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches, M0
     const int l32 = lane & 31, g = lane >> 5;
     const Tile w = locate<BK>(p);
     const Rows r = rows_of(p, w, wave, l32);
-    const int L = p.start_pos + p.T;
-    const uint16_t *kbase = (const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride;
-    const uint16_t *vbase = (const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride;
+    const __amdgpu_buffer_rsrc_t rk =
+        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+
+    // per-lane source offsets (bytes, relative to the tile's first row)
+    int koff[LOADS], voff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int pos = (wave * LOADS + i) * kWave + lane;
+        const int row = pos / CPR, cs = pos % CPR;
+        koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
+        voff[i] = row * D * 2 + ((cs ^ swz_v<CPR>(row)) * 16);
+    }
+#define ISSUE_TILE(kt, buf)                                                                       \
+    do {                                                                                          \
+        const int base_ = (kt) * BK * D * 2;                                                      \
+        uint8_t *kdst_ = smem + (2 * (buf)) * TILE_BYTES + wave * LOADS * 1024;                   \
+        uint8_t *vdst_ = smem + (2 * (buf) + 1) * TILE_BYTES + wave * LOADS * 1024;               \
+        _Pragma("unroll") for (int i_ = 0; i_ < LOADS; ++i_) {                                    \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(kdst_ + i_ * 1024), 16, koff[i_], \
+                                                     base_, 0, 0);                                \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(vdst_ + i_ * 1024), 16, voff[i_], \
+                                                     base_, 0, 0);                                \
+        }                                                                                         \
+    } while (0)
 
     u32x4 qreg[D / 16];
     {
@@ -272,116 +356,103 @@ void attn_fwd16(Params p) {
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -INFINITY, lsum = 0.f;
+    float mref = -INFINITY;          // reference row max, log2 units (raw score * c)
+    float lsum = 0.f;                // this lane's share of the row sum
+    const float c = p.c;
 
-    u32x4 kbuf[KPT];
-    u32x4 vbuf[VPT][2];
-    auto gload = [&](int kt) {
-        const int j0 = kt * BK;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * kThreads;
-            const int key = idx / (D / 8), c8 = idx % (D / 8);
-            const int j = j0 + key;
-            kbuf[i] = j < L ? *(const u32x4 *)(kbase + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * kThreads;
-            if (VTASK < kThreads && idx >= VTASK) break;
-            const int c8 = idx % (D / 8), kp = idx / (D / 8);
-            const int j = j0 + 2 * kp;
-            vbuf[i][0] = j < L ? *(const u32x4 *)(vbase + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
-            vbuf[i][1] = j + 1 < L ? *(const u32x4 *)(vbase + (int64_t)(j + 1) * D + 8 * c8)
-                                   : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * kThreads;
-            const int key = idx / (D / 8), c8 = idx % (D / 8);
-            *(u32x4 *)&Ks[key * KROW + 8 * c8] = kbuf[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * kThreads;
-            if (VTASK < kThreads && idx >= VTASK) break;
-            const int c8 = idx % (D / 8), kp = idx / (D / 8);
-            const u32x4 a = vbuf[i][0], b = vbuf[i][1];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t wa = a[e / 2], wb = b[e / 2];
-                const uint32_t pair = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u))
-                                              : ((wa & 0xffffu) | (wb << 16));
-                *(uint32_t *)&Vt[(8 * c8 + e) * VROW + 2 * kp] = pair;
-            }
-        }
-    };
+    // transposed-read addresses of V (bytes within a V tile), for key0 = 0
+    const int trow = 4 * g + (lane & 15) / 4;                    // + key0
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);     // + d0, elements
 
     if (w.kt_begin < w.kt_end) {
-        if (PREFETCH) gload(w.kt_begin);
+        ISSUE_TILE(w.kt_begin, 0);
+        wait_vmem();
+        __syncthreads();
         for (int kt = w.kt_begin; kt < w.kt_end; ++kt) {
-            if (!PREFETCH) gload(kt);
-            __syncthreads();
-            lstore();
-            __syncthreads();
-            if (PREFETCH && kt + 1 < w.kt_end) gload(kt + 1);
+            const int buf = (kt - w.kt_begin) & 1;
+            if (kt + 1 < w.kt_end) ISSUE_TILE(kt + 1, buf ^ 1);
             const int j0 = kt * BK;
-            if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) continue;
-
-            f32x16 s[BK / 32];
+            if (r.wave_any && j0 <= r.w_pos_max && j0 + BK - 1 >= r.w_lo_min) {
+                const uint8_t *Ks = smem + (2 * buf) * TILE_BYTES;
+                const uint8_t *Vs = smem + (2 * buf + 1) * TILE_BYTES;
+                f32x16 s[BK / 32];
 #pragma unroll
-            for (int b = 0; b < BK / 32; ++b) {
-                s[b] = f32x16{};
-                const uint16_t *kp = &Ks[(32 * b + l32) * KROW + 8 * g];
+                for (int b = 0; b < BK / 32; ++b) {
+                    s[b] = f32x16{};
+                    const int row = 32 * b + l32;
+                    const uint8_t *krow = Ks + row * (CPR * 16);
+                    const int sw = swz_k<CPR>(row);
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-                    s[b] = Ty::mma(*(const u32x4 *)(kp + 16 * ks), qreg[ks], s[b]);
-            }
-            if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+                    for (int ks = 0; ks < D / 16; ++ks)
+                        s[b] = Ty::mma(*(const u32x4 *)(krow + (((2 * ks + g) ^ sw) * 16)), qreg[ks], s[b]);
+                }
+                if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+#pragma unroll
+                    for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
+                            if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                        }
+                }
+                // row max of the tile (raw scores), both lane halves
+                float mt = -INFINITY;
 #pragma unroll
                 for (int b = 0; b < BK / 32; ++b)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
-                        if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                    for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
+                mt = max_halves(mt) * c;
+                // move the reference max only when p could exceed 2^8 (exact either way)
+                if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
+                    const float mnew = fmaxf(mref, mt);
+                    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+                    mref = mnew;
+                    lsum *= alpha;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+                }
+                const float mc = mref == -INFINITY ? 0.f : mref;
+                u32x4 pb[BK / 16];
+#pragma unroll
+                for (int b = 0; b < BK / 32; ++b)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int i0 = 8 * half + 2 * jj;
+                            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
+                            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
+                            const uint32_t pk = Ty::pack(p0, p1);
+                            pb[2 * b + half][jj] = pk;
+                            lsum = Ones::dot(pk, lsum, Ty{});
+                        }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                    for (int ks = 0; ks < BK / 16; ++ks) {
+                        u32x4 a;
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int row = 16 * ks + 8 * hh + trow;
+                            const int d = 32 * db + tcol;
+                            const int addr = row * (CPR * 16) + (((d >> 3) ^ swz_v<CPR>(row)) * 16) + (d & 7) * 2;
+                            const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(Vs + addr));
+                            const u32x2 t2 = __builtin_bit_cast(u32x2, t);
+                            a[2 * hh] = t2[0];
+                            a[2 * hh + 1] = t2[1];
+                        }
+                        o[db] = Ty::mma(a, pb[ks], o[db]);
                     }
-            }
-            float mc;
-            const float alpha = softmax_max<BK / 32>(s, m, p.c, mc);
-            u32x4 pb[BK / 16];
-            float ps = 0.f;
-#pragma unroll
-            for (int b = 0; b < BK / 32; ++b)
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int i0 = 8 * half + 2 * jj;
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], p.c, -mc));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], p.c, -mc));
-                        ps += p0 + p1;
-                        pb[2 * b + half][jj] = Ty::pack(p0, p1);
-                    }
-            lsum = lsum * alpha + ps;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint16_t *vp = &Vt[(32 * db + l32) * VROW + 4 * g];
-#pragma unroll
-                for (int ks = 0; ks < BK / 16; ++ks) {
-                    const u32x2 lo2 = *(const u32x2 *)(vp + 16 * ks);
-                    const u32x2 hi2 = *(const u32x2 *)(vp + 16 * ks + 8);
-                    const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                    o[db] = Ty::mma(a, pb[ks], o[db]);
                 }
             }
+            wait_vmem();
+            __syncthreads();
         }
     }
-    write_rows<D>(p, w, r, g, o, m, lsum);
+    write_rows<D>(p, w, r, g, o, mref, lsum);
+#endif
 }
+#undef ISSUE_TILE
 
 // ---- fp32 kernel ---------------------------------------------------------------
 
@@ -405,7 +476,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
     __shared__ __attribute__((aligned(16))) float Ks[BK * KROW];
     __shared__ __attribute__((aligned(16))) float Vt[D * VROW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches, M0
     const int l32 = lane & 31, g = lane >> 5;
     const Tile w = locate<BK>(p);
     const Rows r = rows_of(p, w, wave, l32);
@@ -538,12 +610,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
             }
         }
     }
-    write_rows<D>(p, w, r, g, o, m, lsum);
+    write_rows<D>(p, w, r, g, o, m * p.c, lsum);
 }
 
 // ---- split merge ------------------------------------------------------------------
 
-// out(t, h, :) = sum_s w_s O_s / sum_s w_s with w_s = l_s * 2^((m_s - m*) c),
+// out(t, h, :) = sum_s w_s O_s / sum_s w_s with w_s = l_s * 2^(m_s - m*) (m in log2 units),
 // m* the largest m_s among splits that saw a valid key (l_s > 0).
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const float2 *ws_ml,
@@ -564,7 +636,7 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
     for (int s = 0; s < S; ++s) {
         const float2 ml = ws_ml[s * rows + row];
         if (ml.y > 0.f) {
-            const float wgt = ml.y * __builtin_amdgcn_exp2f((ml.x - mstar) * c);
+            const float wgt = ml.y * __builtin_amdgcn_exp2f(ml.x - mstar);
             wsum += wgt;
             acc += wgt * *(const f32x4 *)(ws_o + (s * rows + row) * D + 4 * d4);
         }
@@ -585,16 +657,16 @@ struct Variant {
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, attn_fwd16<Bf16, 32, 64, true, 2>},
-    {PA_DTYPE_BF16, 64, 64, 2, attn_fwd16<Bf16, 64, 64, true, 2>},
-    {PA_DTYPE_BF16, 128, 64, 2, attn_fwd16<Bf16, 128, 64, true, 2>},
-    {PA_DTYPE_BF16, 256, 32, 1, attn_fwd16<Bf16, 256, 32, true, 1>},
-    {PA_DTYPE_BF16, 512, 32, 1, attn_fwd16<Bf16, 512, 32, false, 1>},
-    {PA_DTYPE_F16, 32, 64, 2, attn_fwd16<F16, 32, 64, true, 2>},
-    {PA_DTYPE_F16, 64, 64, 2, attn_fwd16<F16, 64, 64, true, 2>},
-    {PA_DTYPE_F16, 128, 64, 2, attn_fwd16<F16, 128, 64, true, 2>},
-    {PA_DTYPE_F16, 256, 32, 1, attn_fwd16<F16, 256, 32, true, 1>},
-    {PA_DTYPE_F16, 512, 32, 1, attn_fwd16<F16, 512, 32, false, 1>},
+    {PA_DTYPE_BF16, 32, 64, 2, attn_fwd16<Bf16, 32, 64, 2>},
+    {PA_DTYPE_BF16, 64, 64, 2, attn_fwd16<Bf16, 64, 64, 2>},
+    {PA_DTYPE_BF16, 128, 64, 2, attn_fwd16<Bf16, 128, 64, 2>},
+    {PA_DTYPE_BF16, 256, 32, 1, attn_fwd16<Bf16, 256, 32, 1>},
+    {PA_DTYPE_BF16, 512, 32, 1, attn_fwd16<Bf16, 512, 32, 1>},
+    {PA_DTYPE_F16, 32, 64, 2, attn_fwd16<F16, 32, 64, 2>},
+    {PA_DTYPE_F16, 64, 64, 2, attn_fwd16<F16, 64, 64, 2>},
+    {PA_DTYPE_F16, 128, 64, 2, attn_fwd16<F16, 128, 64, 2>},
+    {PA_DTYPE_F16, 256, 32, 1, attn_fwd16<F16, 256, 32, 1>},
+    {PA_DTYPE_F16, 512, 32, 1, attn_fwd16<F16, 512, 32, 1>},
     {PA_DTYPE_F32, 32, 32, 2, attn_fwd32<32, 32>},
     {PA_DTYPE_F32, 64, 32, 2, attn_fwd32<64, 32>},
     {PA_DTYPE_F32, 128, 32, 2, attn_fwd32<128, 32>},
@@ -640,6 +712,8 @@ int check_shape(int dtype, int T, int start_pos, int H, int KVH, int D, int wind
     if ((int64_t)start_pos + T > INT32_MAX) return PA_ERR_INVALID_ARG;
     if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16) return PA_ERR_UNSUPPORTED;
     if (H / KVH > kRowsPerGroup) return PA_ERR_UNSUPPORTED;
+    // the 16-bit kernels address one kv head's rows with 32-bit buffer offsets
+    if (dtype != PA_DTYPE_F32 && ((int64_t)start_pos + T) * D * 2 > INT32_MAX) return PA_ERR_UNSUPPORTED;
     if (!find_variant(dtype, D)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -737,7 +811,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.S = pl.S;
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
-    (void)dtype;
+    p.kv_bytes = (int)std::min<int64_t>(((int64_t)start_pos + T) * D * elem_bytes(dtype), INT32_MAX);
     hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(kThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (pl.S > 1) {
