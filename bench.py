@@ -111,6 +111,19 @@ def cpu_baseline(wl, x, target_s: float):
                       f"({rows} per chunk), fp64 oracle, {t:.1f} s wall, {f / 1e9:.1f} GFLOP"}
 
 
+def calibrate_copy(nbytes: int):
+    """A copy kernel of known size: FETCH_SIZE / WRITE_SIZE per dispatch of this
+    kernel, divided by nbytes, is the factor that turns the counters into bytes."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,7 +132,13 @@ def main():
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times "
+                         "(reference for the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

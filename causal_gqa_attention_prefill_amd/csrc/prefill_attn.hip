@@ -49,6 +49,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 
 #include "prefill_attn.h"
@@ -162,21 +163,22 @@ struct Rows {
     int w_pos_min, w_pos_max, w_lo_min, w_lo_max;
 };
 
-__device__ inline Rows rows_of(const Params &p, const Tile &w, int wave, int l32) {
+template <int RPW = kRowsPerWave>
+__device__ inline Rows rows_of(const Params &p, const Tile &w, int wave, int lrow) {
     Rows r;
-    const int n = wave * kRowsPerWave + l32;
+    const int n = wave * RPW + lrow;
     const int tl = n / p.G;
     r.t = w.t0 + tl;
     r.h = w.kvh * p.G + n % p.G;
     r.ok = tl < p.TQ && r.t <= w.t_last;
     r.pos = r.ok ? p.start_pos + r.t : -1;
     r.lo = r.ok ? first_key(r.pos, p.window) : 0;
-    const int tf = w.t0 + (wave * kRowsPerWave) / p.G;
-    const int tl_last = min(w.t0 + (wave * kRowsPerWave + kRowsPerWave - 1) / p.G,
+    const int tf = w.t0 + (wave * RPW) / p.G;
+    const int tl_last = min(w.t0 + (wave * RPW + RPW - 1) / p.G,
                             min(w.t0 + p.TQ - 1, w.t_last));
-    r.wave_any = (wave * kRowsPerWave) / p.G < p.TQ && tf <= w.t_last;
-    r.wave_ragged = (wave * kRowsPerWave + kRowsPerWave - 1) / p.G >= p.TQ ||
-                    w.t0 + (wave * kRowsPerWave + kRowsPerWave - 1) / p.G > w.t_last;
+    r.wave_any = (wave * RPW) / p.G < p.TQ && tf <= w.t_last;
+    r.wave_ragged = (wave * RPW + RPW - 1) / p.G >= p.TQ ||
+                    w.t0 + (wave * RPW + RPW - 1) / p.G > w.t_last;
     r.w_pos_min = p.start_pos + tf;
     r.w_pos_max = p.start_pos + tl_last;
     r.w_lo_min = first_key(r.w_pos_min, p.window);
@@ -304,13 +306,17 @@ void attn_fwd16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
     constexpr int CPR = D / 8;                        // 16-byte chunks per row
+    constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = BK * CPR;
     constexpr int TILE_BYTES = TILE_CHUNKS * 16;
     constexpr int LOADS = TILE_CHUNKS / (kWaves * kWave);   // per wave, per matrix, per tile
     static_assert(LOADS * kWaves * kWave == TILE_CHUNKS, "staging split");
+    constexpr int NB = BK / 32;                       // 32-key blocks per tile
+    constexpr int NKB = D / 16 < 8 ? D / 16 : 8;      // distinct K read bases per lane
+    constexpr int NVB = D / 32 < 4 ? D / 32 : 4;      // distinct V read bases per lane
 
-    // [buffer][K, V][TILE_BYTES]
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE_BYTES];
+    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches, M0
@@ -322,7 +328,7 @@ void attn_fwd16(Params p) {
     const __amdgpu_buffer_rsrc_t rv =
         head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
 
-    // per-lane source offsets (bytes, relative to the tile's first row)
+    // DMA source offsets (bytes, relative to the tile's first row) of this lane
     int koff[LOADS], voff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -331,18 +337,24 @@ void attn_fwd16(Params p) {
         koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
         voff[i] = row * D * 2 + ((cs ^ swz_v<CPR>(row)) * 16);
     }
-#define ISSUE_TILE(kt, buf)                                                                       \
-    do {                                                                                          \
-        const int base_ = (kt) * BK * D * 2;                                                      \
-        uint8_t *kdst_ = smem + (2 * (buf)) * TILE_BYTES + wave * LOADS * 1024;                   \
-        uint8_t *vdst_ = smem + (2 * (buf) + 1) * TILE_BYTES + wave * LOADS * 1024;               \
-        _Pragma("unroll") for (int i_ = 0; i_ < LOADS; ++i_) {                                    \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(kdst_ + i_ * 1024), 16, koff[i_], \
-                                                     base_, 0, 0);                                \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(vdst_ + i_ * 1024), 16, voff[i_], \
-                                                     base_, 0, 0);                                \
-        }                                                                                         \
-    } while (0)
+    // LDS read offsets (bytes within a tile).  K: chunk 2ks+g of row l32 sits at
+    // (2ks+g) ^ swz_k(l32); the swizzle only touches the low four chunk bits, so
+    // step ks = 8u + v reads kbase[v] + 256u.  V: the transposed read of d-block
+    // db at key 0 is vbase[db % 4] + 256 (db / 4), since swz_v only touches chunk
+    // bits 2-3.  Everything else is an immediate offset.
+    int kbase[NKB], vbase[NVB];
+#pragma unroll
+    for (int v = 0; v < NKB; ++v)
+        kbase[v] = l32 * ROW_BYTES + (((2 * v + g) ^ swz_k<CPR>(l32)) * 16);
+    {
+        const int trow = 4 * g + (lane & 15) / 4;
+        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int db = 0; db < NVB; ++db) {
+            const int d = 32 * db + tcol;
+            vbase[db] = trow * ROW_BYTES + (((d >> 3) ^ swz_v<CPR>(trow)) * 16) + (d & 7) * 2;
+        }
+    }
 
     u32x4 qreg[D / 16];
     {
@@ -360,91 +372,104 @@ void attn_fwd16(Params p) {
     float lsum = 0.f;                // this lane's share of the row sum
     const float c = p.c;
 
-    // transposed-read addresses of V (bytes within a V tile), for key0 = 0
-    const int trow = 4 * g + (lane & 15) / 4;                    // + key0
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);     // + d0, elements
+    auto issue = [&](int kt, int kdst, int vdst) {
+        const int base = kt * BK * D * 2;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+        }
+    };
 
-    if (w.kt_begin < w.kt_end) {
-        ISSUE_TILE(w.kt_begin, 0);
+    // one KV tile from the LDS buffers at byte offsets KO (K) and VO (V)
+    auto tile = [&](auto KO_, auto VO_, int kt) {
+        constexpr int KO = decltype(KO_)::value, VO = decltype(VO_)::value;
+        const int j0 = kt * BK;
+        if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) return;
+        f32x16 s[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            s[b] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const uint8_t *a = smem + KO + 32 * b * ROW_BYTES + kbase[ks % NKB] + 256 * (ks / NKB);
+                s[b] = Ty::mma(*(const u32x4 *)a, qreg[ks], s[b]);
+            }
+        }
+        if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
+                    if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                }
+        }
+        // row max of the tile (raw scores), both lane halves
+        float mt = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
+        mt = max_halves(mt) * c;
+        // move the reference max only when p could exceed 2^8 (exact either way)
+        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+            mref = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+        const float mc = mref == -INFINITY ? 0.f : mref;
+        u32x4 pb[BK / 16];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i0 = 8 * half + 2 * jj;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
+                    const uint32_t pk = Ty::pack(p0, p1);
+                    pb[2 * b + half][jj] = pk;
+                    lsum = Ones::dot(pk, lsum, Ty{});
+                }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const uint8_t *a = smem + VO + 16 * ks * ROW_BYTES + vbase[db % NVB] + 256 * (db / NVB);
+                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a));
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a + 8 * ROW_BYTES));
+                const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+                o[db] = Ty::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[ks], o[db]);
+            }
+        }
+    };
+
+    using B0K = std::integral_constant<int, 0>;
+    using B1K = std::integral_constant<int, TILE_BYTES>;
+    using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
+    using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
+    const int kb0 = w.kt_begin, ke = w.kt_end;
+    if (kb0 < ke) {
+        issue(kb0, B0K::value, B0V::value);
         wait_vmem();
         __syncthreads();
-        for (int kt = w.kt_begin; kt < w.kt_end; ++kt) {
-            const int buf = (kt - w.kt_begin) & 1;
-            if (kt + 1 < w.kt_end) ISSUE_TILE(kt + 1, buf ^ 1);
-            const int j0 = kt * BK;
-            if (r.wave_any && j0 <= r.w_pos_max && j0 + BK - 1 >= r.w_lo_min) {
-                const uint8_t *Ks = smem + (2 * buf) * TILE_BYTES;
-                const uint8_t *Vs = smem + (2 * buf + 1) * TILE_BYTES;
-                f32x16 s[BK / 32];
-#pragma unroll
-                for (int b = 0; b < BK / 32; ++b) {
-                    s[b] = f32x16{};
-                    const int row = 32 * b + l32;
-                    const uint8_t *krow = Ks + row * (CPR * 16);
-                    const int sw = swz_k<CPR>(row);
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks)
-                        s[b] = Ty::mma(*(const u32x4 *)(krow + (((2 * ks + g) ^ sw) * 16)), qreg[ks], s[b]);
-                }
-                if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
-#pragma unroll
-                    for (int b = 0; b < BK / 32; ++b)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
-                            if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
-                        }
-                }
-                // row max of the tile (raw scores), both lane halves
-                float mt = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < BK / 32; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
-                mt = max_halves(mt) * c;
-                // move the reference max only when p could exceed 2^8 (exact either way)
-                if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
-                    const float mnew = fmaxf(mref, mt);
-                    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-                    mref = mnew;
-                    lsum *= alpha;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-                }
-                const float mc = mref == -INFINITY ? 0.f : mref;
-                u32x4 pb[BK / 16];
-#pragma unroll
-                for (int b = 0; b < BK / 32; ++b)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            const int i0 = 8 * half + 2 * jj;
-                            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
-                            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
-                            const uint32_t pk = Ty::pack(p0, p1);
-                            pb[2 * b + half][jj] = pk;
-                            lsum = Ones::dot(pk, lsum, Ty{});
-                        }
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                    for (int ks = 0; ks < BK / 16; ++ks) {
-                        u32x4 a;
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            const int row = 16 * ks + 8 * hh + trow;
-                            const int d = 32 * db + tcol;
-                            const int addr = row * (CPR * 16) + (((d >> 3) ^ swz_v<CPR>(row)) * 16) + (d & 7) * 2;
-                            const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(Vs + addr));
-                            const u32x2 t2 = __builtin_bit_cast(u32x2, t);
-                            a[2 * hh] = t2[0];
-                            a[2 * hh + 1] = t2[1];
-                        }
-                        o[db] = Ty::mma(a, pb[ks], o[db]);
-                    }
-                }
-            }
+        for (int kt = kb0; kt < ke; kt += 2) {
+            // tile kt in buffer 0 while tile kt+1 streams into buffer 1
+            if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
+            tile(B0K{}, B0V{}, kt);
+            wait_vmem();
+            __syncthreads();
+            if (kt + 1 >= ke) break;
+            // tile kt+1 in buffer 1 while tile kt+2 streams into buffer 0
+            if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
+            tile(B1K{}, B1V{}, kt + 1);
             wait_vmem();
             __syncthreads();
         }
@@ -452,7 +477,235 @@ void attn_fwd16(Params p) {
     write_rows<D>(p, w, r, g, o, mref, lsum);
 #endif
 }
-#undef ISSUE_TILE
+
+// ---- bf16 / fp16 kernel, 16 rows per wavefront (head_dim 256 and 512) ----------
+//
+// At head_dim 512 one wavefront cannot hold 32 rows of fp32 O (512 registers)
+// next to its Q rows.  Here each of 8 wavefronts owns 16 rows and the
+// products run on v_mfma_f32_16x16x32 (accumulator lane l, register i: row
+// 4*(l/16) + i, column l%16):
+//   S^T block (16 keys x 16 rows) = K Q^T, k = head_dim in steps of 32;
+//   each lane holds 4 keys of one row per block, so the row max and sum
+//   combine the four lane groups (l/16) with two exchanges;
+//   O^T block (16 d x 16 rows) += V^T P^T, k = 32 keys: P comes from two S^T
+//   blocks in the B-operand layout (slot (l/16, j): key 16*(j/4) + 4*(l/16) +
+//   j%4), V^T from two transposed LDS reads.
+// The V tile is swizzled for those reads: chunk c of row r sits at
+// c ^ (2 * (r % 8)), so the 8 rows x 32 bytes a half-wave reads per
+// transposed load fall in 16 different bank groups.
+
+constexpr int kWaves16 = 8;
+constexpr int kThreads16 = kWaves16 * kWave;
+constexpr int kRowsPerWave16 = 16;
+static_assert(kWaves16 * kRowsPerWave16 == kRowsPerGroup, "same rows per work-group");
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+struct Bf16m16 {
+    __device__ static inline f32x4v mma(u32x4 a, u32x4 b, f32x4v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+struct F16m16 {
+    __device__ static inline f32x4v mma(u32x4 a, u32x4 b, f32x4v c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+template <class Ty> struct M16;
+template <> struct M16<Bf16> { using T = Bf16m16; };
+template <> struct M16<F16> { using T = F16m16; };
+
+template <int CPR>
+__device__ inline int swz_v16(int row) {
+    static_assert(CPR >= 16, "head_dim >= 128");
+    return 2 * (row & 7);
+}
+
+template <class Ty, int D, int BK>
+__global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd16_r16(Params p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(D >= 128 && D % 32 == 0 && BK % 32 == 0, "tile shape");
+    using MM = typename M16<Ty>::T;
+    constexpr int CPR = D / 8;
+    constexpr int ROW_BYTES = CPR * 16;
+    constexpr int TILE_CHUNKS = BK * CPR;
+    constexpr int TILE_BYTES = TILE_CHUNKS * 16;
+    constexpr int LOADS = TILE_CHUNKS / (kWaves16 * kWave);
+    static_assert(LOADS * kWaves16 * kWave == TILE_CHUNKS, "staging split");
+    constexpr int NKS = D / 32;                       // k steps of S
+    constexpr int NDB = D / 16;                       // 16-wide d blocks of O
+    constexpr int NSB = BK / 16;                      // 16-key blocks of S per tile
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const Tile w = locate<BK>(p);
+    const Rows r = rows_of<kRowsPerWave16>(p, w, wave, l16);
+    const __amdgpu_buffer_rsrc_t rk =
+        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+
+    int koff[LOADS], voff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int pos = (wave * LOADS + i) * kWave + lane;
+        const int row = pos / CPR, cs = pos % CPR;
+        koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
+        voff[i] = row * D * 2 + ((cs ^ swz_v16<CPR>(row)) * 16);
+    }
+    // K: chunk 4ks + g4 of row 16b + l16 sits at (4ks + g4) ^ l16: the XOR only
+    // touches chunk bits 0-3, so step ks = 4u + v reads kbase[v] + 256u.
+    // V: transposed read of d-block db at key 0: rows 4*g4 + (lane%16)/4, d =
+    // 16 db + 4 (lane%4); the XOR 2*(row%8) touches chunk bits 1-3, so
+    // block db = 8u + v reads vbase[v] + 256u.
+    int kbase[4], vbase[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) kbase[v] = l16 * ROW_BYTES + (((4 * v + g4) ^ swz_k<CPR>(l16)) * 16);
+    {
+        const int trow = 4 * g4 + l16 / 4;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const int d = 16 * v + 4 * (lane & 3);
+            vbase[v] = trow * ROW_BYTES + (((d >> 3) ^ swz_v16<CPR>(trow)) * 16) + (d & 7) * 2;
+        }
+    }
+
+    u32x4 qreg[NKS];
+    {
+        const uint16_t *qp = (const uint16_t *)p.q + (int64_t)(r.ok ? r.t : 0) * p.q_row_stride +
+                             (int64_t)r.h * D + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qreg[ks] = r.ok ? *(const u32x4 *)(qp + 32 * ks) : u32x4{0, 0, 0, 0};
+    }
+
+    f32x4v o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    float mref = -INFINITY, lsum = 0.f;
+    const float c = p.c;
+
+    auto issue = [&](int kt, int kdst, int vdst) {
+        const int base = kt * BK * D * 2;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+        }
+    };
+
+    auto tile = [&](auto KO_, auto VO_, int kt) {
+        constexpr int KO = decltype(KO_)::value, VO = decltype(VO_)::value;
+        const int j0 = kt * BK;
+        if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) return;
+        f32x4v s[NSB];
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) {
+            s[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint8_t *a = smem + KO + 16 * b * ROW_BYTES + kbase[ks % 4] + 256 * (ks / 4);
+                s[b] = MM::mma(*(const u32x4 *)a, qreg[ks], s[b]);
+            }
+        }
+        if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
+#pragma unroll
+            for (int b = 0; b < NSB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = j0 + 16 * b + 4 * g4 + i;
+                    if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
+                }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NSB; ++b) mt = fmaxf(mt, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+            mref = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+        const float mc = mref == -INFINITY ? 0.f : mref;
+        u32x4 pb[BK / 32];
+#pragma unroll
+        for (int kp = 0; kp < BK / 32; ++kp)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const f32x4v &sb = s[2 * kp + half];
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[2 * jj], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[2 * jj + 1], c, -mc));
+                    const uint32_t pk = Ty::pack(p0, p1);
+                    pb[kp][2 * half + jj] = pk;
+                    lsum = Ones::dot(pk, lsum, Ty{});
+                }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int kp = 0; kp < BK / 32; ++kp) {
+                const uint8_t *a = smem + VO + 32 * kp * ROW_BYTES + vbase[db % 8] + 256 * (db / 8);
+                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a));
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a + 16 * ROW_BYTES));
+                const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+                o[db] = MM::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[kp], o[db]);
+            }
+        }
+    };
+
+    using B0K = std::integral_constant<int, 0>;
+    using B1K = std::integral_constant<int, TILE_BYTES>;
+    using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
+    using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
+    const int kb0 = w.kt_begin, ke = w.kt_end;
+    if (kb0 < ke) {
+        issue(kb0, B0K::value, B0V::value);
+        wait_vmem();
+        __syncthreads();
+        for (int kt = kb0; kt < ke; kt += 2) {
+            if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
+            tile(B0K{}, B0V{}, kt);
+            wait_vmem();
+            __syncthreads();
+            if (kt + 1 >= ke) break;
+            if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
+            tile(B1K{}, B1V{}, kt + 1);
+            wait_vmem();
+            __syncthreads();
+        }
+    }
+
+    // the row's sum is spread over the four lane groups
+    float ltot = lsum + __shfl_xor(lsum, 16);
+    ltot = ltot + __shfl_xor(ltot, 32);
+    if (!r.ok) return;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float *dst;
+    if (p.S == 1) {
+        dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+    } else {
+        const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
+        dst = p.ws_o + row * D + 4 * g4;
+        if (g4 == 0) p.ws_ml[row] = make_float2(mref, ltot);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+        *(f32x4 *)(dst + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+#endif
+}
 
 // ---- fp32 kernel ---------------------------------------------------------------
 
@@ -653,24 +906,25 @@ using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, i
 struct Variant {
     int dtype, D, BK;
     int groups_per_cu;         // resident work-groups per CU the kernel is sized for
+    int threads;               // work-group size (4 or 8 wavefronts)
     KernelFn fn;
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, attn_fwd16<Bf16, 32, 64, 2>},
-    {PA_DTYPE_BF16, 64, 64, 2, attn_fwd16<Bf16, 64, 64, 2>},
-    {PA_DTYPE_BF16, 128, 64, 2, attn_fwd16<Bf16, 128, 64, 2>},
-    {PA_DTYPE_BF16, 256, 32, 1, attn_fwd16<Bf16, 256, 32, 1>},
-    {PA_DTYPE_BF16, 512, 32, 1, attn_fwd16<Bf16, 512, 32, 1>},
-    {PA_DTYPE_F16, 32, 64, 2, attn_fwd16<F16, 32, 64, 2>},
-    {PA_DTYPE_F16, 64, 64, 2, attn_fwd16<F16, 64, 64, 2>},
-    {PA_DTYPE_F16, 128, 64, 2, attn_fwd16<F16, 128, 64, 2>},
-    {PA_DTYPE_F16, 256, 32, 1, attn_fwd16<F16, 256, 32, 1>},
-    {PA_DTYPE_F16, 512, 32, 1, attn_fwd16<F16, 512, 32, 1>},
-    {PA_DTYPE_F32, 32, 32, 2, attn_fwd32<32, 32>},
-    {PA_DTYPE_F32, 64, 32, 2, attn_fwd32<64, 32>},
-    {PA_DTYPE_F32, 128, 32, 2, attn_fwd32<128, 32>},
-    {PA_DTYPE_F32, 256, 32, 1, attn_fwd32<256, 32>},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, attn_fwd16<Bf16, 32, 64, 2>},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, attn_fwd16<Bf16, 64, 64, 2>},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, attn_fwd16<Bf16, 128, 64, 2>},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, attn_fwd16_r16<Bf16, 256, 64>},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, attn_fwd16_r16<Bf16, 512, 32>},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, attn_fwd16<F16, 32, 64, 2>},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, attn_fwd16<F16, 64, 64, 2>},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, attn_fwd16<F16, 128, 64, 2>},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, attn_fwd16_r16<F16, 256, 64>},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, attn_fwd16_r16<F16, 512, 32>},
+    {PA_DTYPE_F32, 32, 32, 2, kThreads, attn_fwd32<32, 32>},
+    {PA_DTYPE_F32, 64, 32, 2, kThreads, attn_fwd32<64, 32>},
+    {PA_DTYPE_F32, 128, 32, 2, kThreads, attn_fwd32<128, 32>},
+    {PA_DTYPE_F32, 256, 32, 1, kThreads, attn_fwd32<256, 32>},
 };
 
 MergeFn merge_for(int D) {
@@ -812,7 +1066,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
     p.kv_bytes = (int)std::min<int64_t>(((int64_t)start_pos + T) * D * elem_bytes(dtype), INT32_MAX);
-    hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(pl.var->threads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (pl.S > 1) {
         const int64_t n = (int64_t)T * H * (D / 4);
@@ -951,7 +1205,7 @@ int prefill_attn_plan(int dtype, int T, int start_pos, int num_heads, int num_kv
     Plan pl;
     const int st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl);
     if (st != PA_OK) return st;
-    const int64_t vals[8] = {pl.TQ, pl.nq, pl.S, pl.items, pl.var->BK, kWaves,
+    const int64_t vals[8] = {pl.TQ, pl.nq, pl.S, pl.items, pl.var->BK, pl.var->threads / kWave,
                              (int64_t)pl.ws_bytes, pl.tiles};
     for (int i = 0; i < n && i < 8 && info; ++i) info[i] = vals[i];
     return PA_OK;

@@ -85,7 +85,7 @@ def test_plan_shapes():
     p = pa.plan("bf16", 2048, 6144, 32, 8, 128)
     assert p["tokens_per_tile"] * 4 == 128 and p["query_tiles"] == 64
     assert p["workgroups"] == 64 * 8 * p["kv_splits"]
-    assert p["waves_per_workgroup"] == 4
+    assert p["waves_per_workgroup"] in (4, 8)
     # every (tile, kv head) visits only KV tiles that hold a valid key of one of its rows
     bk = p["keys_per_tile"]
     tiles = 0
