@@ -1,0 +1,62 @@
+"""Host-side logic pinned to figures the pages print (CPU only)."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_flop_count_matches_gnosis_figure():
+    g = json.load(open(os.path.join(GOLDEN, "gnosis_mistral_prefill_work.json")))
+    assert g["num_heads"] // g["num_kv_heads"] == g["num_kv_groups"]
+    # bench counts both products (4 flops per valid pair and dim); the page
+    # counts the score product only (2), over all layers
+    per_layer = bench.attention_flops(g["prompt_tokens"], 0, g["num_heads"], g["head_dim"], 0) / 2
+    total_gflop = per_layer * g["layers"] / 1e9
+    assert abs(total_gflop - g["attention_gflop_page"]) <= g["attention_gflop_tolerance"], total_gflop
+
+
+def test_valid_pairs_closed_forms():
+    # causal from 0: T (T + 1) / 2; late chunk: T * start_pos + T (T + 1) / 2
+    assert bench.valid_pairs(2048, 0, 0) == 2048 * 2049 // 2
+    assert bench.valid_pairs(2048, 6144, 0) == 2048 * 6144 + 2048 * 2049 // 2
+    # a window shorter than start_pos keeps exactly `window` keys per row
+    assert bench.valid_pairs(2048, 129024, 1024) == 2048 * 1024
+    # window 1 keeps one key per row
+    assert bench.valid_pairs(77, 5, 1) == 77
+
+
+def test_workloads_follow_the_pages():
+    pad = json.load(open(os.path.join(GOLDEN, "tensorsharp_gemma_padding.json")))
+    g = workloads.WORKLOADS["gemma_global_bf16"]
+    T, sp = g.chunks[0]
+    assert g.head_dim == pad["head_dim"] and T == pad["chunk_tokens"]
+    assert (sp + T) % pad["kv_pad_multiple"] == 0
+    assert abs(sp - pad["late_chunk_start_pos_approx"]) < 2048
+    m = workloads.WORKLOADS["mistral_f32"]
+    gn = json.load(open(os.path.join(GOLDEN, "gnosis_mistral_prefill_work.json")))
+    assert (m.num_heads, m.num_kv_heads, m.head_dim, m.chunks[0][0]) == (
+        gn["num_heads"], gn["num_kv_heads"], gn["head_dim"], gn["prompt_tokens"])
+    c = workloads.WORKLOADS["mistral_bf16_chunked"]
+    assert [sp for _, sp in c.chunks] == [0, 2048, 4096, 6144] and c.capacity == 8192
+
+
+def test_inputs_are_seeded_and_rounded():
+    wl = workloads.WORKLOADS["tiny_f32"]
+    a, b = workloads.make_inputs(wl), workloads.make_inputs(wl)
+    assert (a.q_f32 == b.q_f32).all() and (a.k_f32 == b.k_f32).all()
+    x = workloads.make_random(2, 1, 32, 5, 3, dtype="bf16", seed=4)
+    # the fp32 image is exactly the bf16 value
+    assert (workloads.round_to_bf16_bits(x.k_f32) == x.k_store).all()
+    y = workloads.make_random(2, 1, 32, 5, 3, dtype="f16", seed=4)
+    import numpy as np
+    assert (y.k_store.view(np.float16).astype(np.float32) == y.k_f32).all()
+
+
+def test_bench_refuses_several_gpus():
+    p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert p.returncode == 2 and "one GPU" in p.stderr
