@@ -88,6 +88,9 @@ struct Params {
     int n_items;      // nq * KVH * S work-groups
     float c;          // log2(e) / sqrt(head_dim)
     int kv_bytes;     // bytes of the L valid rows of one kv head (16-bit kernels)
+    const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
+    int vop_kt_lo;         // first KV tile held in vop
+    int vop_tiles;         // KV tiles per kv head held in vop
 };
 
 // ---- storage types ---------------------------------------------------------
@@ -300,6 +303,69 @@ struct Ones {
 
 [[maybe_unused]] constexpr float kRescaleLog2 = 8.f;   // keep a stale row max while p <= 2^8
 
+// ---- V in MFMA operand order ----------------------------------------------------
+//
+// The P.V product contracts over keys, so its A operand wants, per lane, eight
+// keys of one head_dim column: a column of the row-major V cache.  LDS
+// transposed reads deliver that at a third of the plain 128-bit read rate on
+// gfx950, which made them the kernel's bottleneck.  This pass rewrites the V
+// rows of the call's KV tiles once per call, in the order the operands are
+// consumed: for each KV tile, each 16-byte chunk c = (block * steps + step) *
+// 64 + lane holds the 8 values that lane feeds to one MFMA, so the attention
+// kernels copy tiles into LDS verbatim and read each operand with one
+// contiguous ds_read_b128.  Keys at or past L are written as zeros.
+//   M32 (32x32x16 MFMA): block = 32-wide d block, step = 16 keys; lane
+//        (l%32, l/32), element e: key 16*step + 8*(e/4) + 4*(l/32) + e%4,
+//        d = 32*block + l%32
+//   M16 (16x16x32 MFMA): block = 16-wide d block, step = 32 keys; lane
+//        (l%16, l/16), element e: key 32*step + 16*(e/4) + 4*(l/16) + e%4,
+//        d = 16*block + l%16
+template <int D, int BK, bool M16>
+__global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_t kv_head_stride,
+                                                       int L, int kt_lo, int ntiles, uint16_t *vop) {
+    constexpr int PITCH = D + 2;               // LDS row pitch (elements): column reads spread banks
+    constexpr int CHUNKS = BK * D / 8;
+    __shared__ uint32_t t32[BK * PITCH / 2];
+    const uint16_t *t16 = (const uint16_t *)t32;
+    const int tile = blockIdx.x, kvh = blockIdx.y;
+    const int j0 = (kt_lo + tile) * BK;
+    const uint16_t *src = v + (int64_t)kvh * kv_head_stride;
+    for (int cidx = threadIdx.x; cidx < CHUNKS; cidx += 256) {
+        const int key = cidx / (D / 8), c8 = cidx % (D / 8);
+        const int j = j0 + key;
+        const u32x4 val = j < L ? *(const u32x4 *)(src + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
+        uint32_t *row = t32 + (key * PITCH + 8 * c8) / 2;
+        row[0] = val[0];
+        row[1] = val[1];
+        row[2] = val[2];
+        row[3] = val[3];
+    }
+    __syncthreads();
+    uint16_t *dst = vop + ((int64_t)kvh * ntiles + tile) * (BK * D);
+    for (int oc = threadIdx.x; oc < CHUNKS; oc += 256) {
+        const int lane = oc % 64, op = oc / 64;
+        int d, kbase, khalf;
+        if (M16) {
+            const int db = op / (BK / 32), kp = op % (BK / 32);
+            d = 16 * db + (lane & 15);
+            kbase = 32 * kp + 4 * (lane >> 4);
+            khalf = 16;
+        } else {
+            const int db = op / (BK / 16), ks = op % (BK / 16);
+            d = 32 * db + (lane & 31);
+            kbase = 16 * ks + 4 * (lane >> 5);
+            khalf = 8;
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int k0 = kbase + khalf * (e / 4) + (e % 4);
+            w[e / 2] = (uint32_t)t16[k0 * PITCH + d] | ((uint32_t)t16[(k0 + 1) * PITCH + d] << 16);
+        }
+        *(u32x4 *)(dst + 8 * oc) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
 template <class Ty, int D, int BK, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
@@ -313,7 +379,6 @@ void attn_fwd16(Params p) {
     static_assert(LOADS * kWaves * kWave == TILE_CHUNKS, "staging split");
     constexpr int NB = BK / 32;                       // 32-key blocks per tile
     constexpr int NKB = D / 16 < 8 ? D / 16 : 8;      // distinct K read bases per lane
-    constexpr int NVB = D / 32 < 4 ? D / 32 : 4;      // distinct V read bases per lane
 
     // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
@@ -326,7 +391,7 @@ void attn_fwd16(Params p) {
     const __amdgpu_buffer_rsrc_t rk =
         head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
     const __amdgpu_buffer_rsrc_t rv =
-        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+        head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES);
 
     // DMA source offsets (bytes, relative to the tile's first row) of this lane
     int koff[LOADS], voff[LOADS];
@@ -335,26 +400,17 @@ void attn_fwd16(Params p) {
         const int pos = (wave * LOADS + i) * kWave + lane;
         const int row = pos / CPR, cs = pos % CPR;
         koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
-        voff[i] = row * D * 2 + ((cs ^ swz_v<CPR>(row)) * 16);
+        voff[i] = pos * 16;                           // operand-ordered V: verbatim copy
     }
     // LDS read offsets (bytes within a tile).  K: chunk 2ks+g of row l32 sits at
     // (2ks+g) ^ swz_k(l32); the swizzle only touches the low four chunk bits, so
-    // step ks = 8u + v reads kbase[v] + 256u.  V: the transposed read of d-block
-    // db at key 0 is vbase[db % 4] + 256 (db / 4), since swz_v only touches chunk
-    // bits 2-3.  Everything else is an immediate offset.
-    int kbase[NKB], vbase[NVB];
+    // step ks = 8u + v reads kbase[v] + 256u.  V: operand (db, ks) of this lane
+    // is chunk (db * BK/16 + ks) * 64 + lane.  Everything else is an immediate.
+    int kbase[NKB];
 #pragma unroll
     for (int v = 0; v < NKB; ++v)
         kbase[v] = l32 * ROW_BYTES + (((2 * v + g) ^ swz_k<CPR>(l32)) * 16);
-    {
-        const int trow = 4 * g + (lane & 15) / 4;
-        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int db = 0; db < NVB; ++db) {
-            const int d = 32 * db + tcol;
-            vbase[db] = trow * ROW_BYTES + (((d >> 3) ^ swz_v<CPR>(trow)) * 16) + (d & 7) * 2;
-        }
-    }
+    const int vlane = lane * 16;
 
     u32x4 qreg[D / 16];
     {
@@ -374,12 +430,13 @@ void attn_fwd16(Params p) {
 
     auto issue = [&](int kt, int kdst, int vdst) {
         const int base = kt * BK * D * 2;
+        const int vbase_t = (kt - p.vop_kt_lo) * TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
         }
     };
 
@@ -442,11 +499,8 @@ void attn_fwd16(Params p) {
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
-                const uint8_t *a = smem + VO + 16 * ks * ROW_BYTES + vbase[db % NVB] + 256 * (db / NVB);
-                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a));
-                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a + 8 * ROW_BYTES));
-                const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
-                o[db] = Ty::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[ks], o[db]);
+                const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 16) + ks) * 1024 + vlane);
+                o[db] = Ty::mma(a, pb[ks], o[db]);
             }
         }
     };
@@ -549,7 +603,7 @@ void attn_fwd16_r16(Params p) {
     const __amdgpu_buffer_rsrc_t rk =
         head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
     const __amdgpu_buffer_rsrc_t rv =
-        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+        head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES);
 
     int koff[LOADS], voff[LOADS];
 #pragma unroll
@@ -557,24 +611,15 @@ void attn_fwd16_r16(Params p) {
         const int pos = (wave * LOADS + i) * kWave + lane;
         const int row = pos / CPR, cs = pos % CPR;
         koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
-        voff[i] = row * D * 2 + ((cs ^ swz_v16<CPR>(row)) * 16);
+        voff[i] = pos * 16;                           // operand-ordered V: verbatim copy
     }
     // K: chunk 4ks + g4 of row 16b + l16 sits at (4ks + g4) ^ l16: the XOR only
     // touches chunk bits 0-3, so step ks = 4u + v reads kbase[v] + 256u.
-    // V: transposed read of d-block db at key 0: rows 4*g4 + (lane%16)/4, d =
-    // 16 db + 4 (lane%4); the XOR 2*(row%8) touches chunk bits 1-3, so
-    // block db = 8u + v reads vbase[v] + 256u.
-    int kbase[4], vbase[8];
+    // V: operand (db, kp) of this lane is chunk (db * BK/32 + kp) * 64 + lane.
+    int kbase[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) kbase[v] = l16 * ROW_BYTES + (((4 * v + g4) ^ swz_k<CPR>(l16)) * 16);
-    {
-        const int trow = 4 * g4 + l16 / 4;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int d = 16 * v + 4 * (lane & 3);
-            vbase[v] = trow * ROW_BYTES + (((d >> 3) ^ swz_v16<CPR>(trow)) * 16) + (d & 7) * 2;
-        }
-    }
+    const int vlane = lane * 16;
 
     u32x4 qreg[NKS];
     {
@@ -593,12 +638,13 @@ void attn_fwd16_r16(Params p) {
 
     auto issue = [&](int kt, int kdst, int vdst) {
         const int base = kt * BK * D * 2;
+        const int vbase_t = (kt - p.vop_kt_lo) * TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
         }
     };
 
@@ -657,11 +703,8 @@ void attn_fwd16_r16(Params p) {
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int kp = 0; kp < BK / 32; ++kp) {
-                const uint8_t *a = smem + VO + 32 * kp * ROW_BYTES + vbase[db % 8] + 256 * (db / 8);
-                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a));
-                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a + 16 * ROW_BYTES));
-                const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
-                o[db] = MM::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[kp], o[db]);
+                const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 32) + kp) * 1024 + vlane);
+                o[db] = MM::mma(a, pb[kp], o[db]);
             }
         }
     };
@@ -901,6 +944,7 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
 // ---- host side -----------------------------------------------------------------------
 
 using KernelFn = void (*)(Params);
+using PackFn = void (*)(const uint16_t *, int64_t, int, int, int, uint16_t *);
 using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
 
 struct Variant {
@@ -908,23 +952,24 @@ struct Variant {
     int groups_per_cu;         // resident work-groups per CU the kernel is sized for
     int threads;               // work-group size (4 or 8 wavefronts)
     KernelFn fn;
+    PackFn pack;               // V operand-order pass (16-bit inputs), else null
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, kThreads, attn_fwd16<Bf16, 32, 64, 2>},
-    {PA_DTYPE_BF16, 64, 64, 2, kThreads, attn_fwd16<Bf16, 64, 64, 2>},
-    {PA_DTYPE_BF16, 128, 64, 2, kThreads, attn_fwd16<Bf16, 128, 64, 2>},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, attn_fwd16_r16<Bf16, 256, 64>},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, attn_fwd16_r16<Bf16, 512, 32>},
-    {PA_DTYPE_F16, 32, 64, 2, kThreads, attn_fwd16<F16, 32, 64, 2>},
-    {PA_DTYPE_F16, 64, 64, 2, kThreads, attn_fwd16<F16, 64, 64, 2>},
-    {PA_DTYPE_F16, 128, 64, 2, kThreads, attn_fwd16<F16, 128, 64, 2>},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, attn_fwd16_r16<F16, 256, 64>},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, attn_fwd16_r16<F16, 512, 32>},
-    {PA_DTYPE_F32, 32, 32, 2, kThreads, attn_fwd32<32, 32>},
-    {PA_DTYPE_F32, 64, 32, 2, kThreads, attn_fwd32<64, 32>},
-    {PA_DTYPE_F32, 128, 32, 2, kThreads, attn_fwd32<128, 32>},
-    {PA_DTYPE_F32, 256, 32, 1, kThreads, attn_fwd32<256, 32>},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, attn_fwd16<Bf16, 32, 64, 2>, pack_v_operands<32, 64, false>},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, attn_fwd16<Bf16, 64, 64, 2>, pack_v_operands<64, 64, false>},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, attn_fwd16<Bf16, 128, 64, 2>, pack_v_operands<128, 64, false>},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, attn_fwd16_r16<Bf16, 256, 64>, pack_v_operands<256, 64, true>},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, attn_fwd16_r16<Bf16, 512, 32>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, attn_fwd16<F16, 32, 64, 2>, pack_v_operands<32, 64, false>},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, attn_fwd16<F16, 64, 64, 2>, pack_v_operands<64, 64, false>},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, attn_fwd16<F16, 128, 64, 2>, pack_v_operands<128, 64, false>},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, attn_fwd16_r16<F16, 256, 64>, pack_v_operands<256, 64, true>},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, attn_fwd16_r16<F16, 512, 32>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F32, 32, 32, 2, kThreads, attn_fwd32<32, 32>, nullptr},
+    {PA_DTYPE_F32, 64, 32, 2, kThreads, attn_fwd32<64, 32>, nullptr},
+    {PA_DTYPE_F32, 128, 32, 2, kThreads, attn_fwd32<128, 32>, nullptr},
+    {PA_DTYPE_F32, 256, 32, 1, kThreads, attn_fwd32<256, 32>, nullptr},
 };
 
 MergeFn merge_for(int D) {
@@ -950,7 +995,9 @@ struct Plan {
     const Variant *var;
     int G, TQ, nq, S, items;
     int64_t tiles;               // KV tiles visited by all work-groups
-    size_t ws_bytes, ws_ml_offset;
+    int vop_kt_lo, vop_tiles;    // KV tiles rewritten in operand order (16-bit inputs)
+    size_t vop_bytes;            // their bytes, at the start of the workspace
+    size_t ws_bytes, ws_o_offset, ws_ml_offset;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1027,14 +1074,24 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
         tiles += ke - kb;
     }
     pl->tiles = tiles * KVH;
+    pl->vop_kt_lo = 0;
+    pl->vop_tiles = 0;
+    pl->vop_bytes = 0;
+    if (var->pack) {
+        pl->vop_kt_lo = first_key_host(start_pos, window) / var->BK;
+        pl->vop_tiles = (int)(((int64_t)start_pos + T - 1) / var->BK + 1 - pl->vop_kt_lo);
+        const int64_t tile_bytes = (int64_t)var->BK * D * 2;
+        if ((int64_t)pl->vop_tiles * tile_bytes > INT32_MAX) return PA_ERR_UNSUPPORTED;
+        pl->vop_bytes = (size_t)(((int64_t)KVH * pl->vop_tiles * tile_bytes + 255) & ~(int64_t)255);
+    }
+    pl->ws_o_offset = pl->vop_bytes;
+    pl->ws_ml_offset = pl->vop_bytes;
+    pl->ws_bytes = pl->vop_bytes;
     if (pl->S > 1) {
         const size_t rows = (size_t)T * H;
         const size_t o_bytes = (size_t)pl->S * rows * D * sizeof(float);
-        pl->ws_ml_offset = (o_bytes + 255) & ~(size_t)255;
+        pl->ws_ml_offset = pl->ws_o_offset + ((o_bytes + 255) & ~(size_t)255);
         pl->ws_bytes = pl->ws_ml_offset + (size_t)pl->S * rows * sizeof(float2);
-    } else {
-        pl->ws_ml_offset = 0;
-        pl->ws_bytes = 0;
     }
     return PA_OK;
 }
@@ -1049,8 +1106,11 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.k = k;
     p.v = v;
     p.out = out;
-    p.ws_o = pl.S > 1 ? (float *)ws : nullptr;
+    p.ws_o = pl.S > 1 ? (float *)((char *)ws + pl.ws_o_offset) : nullptr;
     p.ws_ml = pl.S > 1 ? (float2 *)((char *)ws + pl.ws_ml_offset) : nullptr;
+    p.vop = pl.var->pack ? (const uint16_t *)ws : nullptr;
+    p.vop_kt_lo = pl.vop_kt_lo;
+    p.vop_tiles = pl.vop_tiles;
     p.q_row_stride = q_row_stride;
     p.kv_head_stride = kv_head_stride;
     p.out_row_stride = out_row_stride;
@@ -1066,6 +1126,12 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
     p.kv_bytes = (int)std::min<int64_t>(((int64_t)start_pos + T) * D * elem_bytes(dtype), INT32_MAX);
+    if (pl.var->pack) {
+        hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream,
+                           (const uint16_t *)v, kv_head_stride, start_pos + T, pl.vop_kt_lo,
+                           pl.vop_tiles, (uint16_t *)ws);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    }
     hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(pl.var->threads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (pl.S > 1) {

@@ -82,11 +82,12 @@ extern "C" {
 /*
  * Packed entry points: q [T][num_heads][head_dim], caches
  * [num_kv_heads][L][head_dim] with L = start_pos + T, out [T][num_heads][head_dim].
- * When the launch needs scratch memory for split-KV partial results the
- * library takes it from a per-device buffer it allocates on first need and
- * grows (hipMalloc; growing synchronises the device once).  Calls that run
- * concurrently on one device share that buffer and must be ordered on one
- * stream.
+ * Scratch memory (bf16/fp16 inputs: a copy of the call's V rows rearranged
+ * into matrix-core operand order; every dtype: split-KV partial results when
+ * the keys are split) comes from a per-device buffer the library allocates on
+ * first need and grows (hipMalloc; growing synchronises the device once).
+ * Calls that run concurrently on one device share that buffer and must be
+ * ordered on one stream.
  */
 int prefill_attn_f32(const float *q, const float *k_cache, const float *v_cache, float *out,
                      int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
