@@ -20,6 +20,10 @@ FLAGS = [
     "-fno-honor-nans",
     # packed-fp32 VALU instructions stay off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in architectural VGPRs: the softmax reads the score
+    # accumulators with VALU, so keeping them out of AGPRs avoids copies and
+    # spills (Q and O, used only by MFMAs, can still go to AGPRs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
