@@ -266,6 +266,10 @@ __device__ inline float softmax_max(const f32x16 (&s)[NB], float &m, float c, fl
 // q+8, q+12, so lanes that address rows (key0 + 4*(l/32) + j/4) at column
 // (d0 + 16*((l/16)%2) + 4*(j%4)), j = l%16, receive
 // V[key0 + 4*(l/32) + r][d0 + l%32], r = 0..3: the A operand of V^T P^T.
+// Operand reads run a few MFMAs ahead of their use (explicitly waited asm
+// reads, see below), and the two S chains of a tile alternate so that each
+// MFMA's accumulator was written two MFMAs earlier.  The row max of a tile
+// combines the two lane halves with a lane swap instead of an LDS exchange.
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -279,6 +283,54 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bytes) 
 #endif
 
 [[maybe_unused]] __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// LDS operand reads issued as inline assembly.  The wait-count pass treats
+// the builtin transposed read as one that may alias any LDS DMA still in
+// flight and puts a vmcnt(0) in front of it, which would stall every P.V
+// phase until the next tile's DMA (bound for the other buffer) has landed.
+// The asm forms are invisible to that pass; their results are waited for
+// with lds_wait, which ties the destination registers so that no user can be
+// scheduled above the wait.
+template <int OFF>
+__device__ inline u32x2 ds_read_tr16(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ inline u32x4 ds_read_b128_asm(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+// Wait until at most N LDS operations of this wave are outstanding.  LDS
+// operations return in order, so every read issued before the last N has
+// landed (other lgkm traffic in between only makes the wait stricter).
+template <int N>
+__device__ inline void lds_wait(u32x2 &a, u32x2 &b) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int N>
+__device__ inline void lds_wait(u32x4 &a) {
+    static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+// Maximum over the two 32-lane halves of a wave without an LDS round trip:
+// the swap leaves x[l] and x[l ^ 32] in the two results of every lane.
+[[maybe_unused]] __device__ inline float max_halves_swap(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int I, int N, class F>
+__device__ inline void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 template <int CPR>
 __device__ inline int swz_k(int row) {
@@ -370,7 +422,7 @@ __global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_
     }
 }
 
-template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD, int STAGES>
+template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -385,9 +437,8 @@ void attn_fwd16(Params p) {
     constexpr int NKB = D / 16 < 8 ? D / 16 : 8;      // distinct K read bases per lane
     constexpr int NVB = D / 32 < 4 ? D / 32 : 4;      // distinct V read bases per lane
 
-    // [K buffer 0 .. STAGES-1][V buffer 0 .. STAGES-1]
-    static_assert(STAGES == 2 || STAGES == 3, "stages");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGES * TILE_BYTES];
+    // [K buffer 0, K buffer 1][V buffer 0, V buffer 1]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches, M0
@@ -426,6 +477,15 @@ void attn_fwd16(Params p) {
             vbase[db] = trow * ROW_BYTES + (((d >> 3) ^ swz_v<CPR>(trow)) * 16) + (d & 7) * 2;
         }
     }
+    constexpr int PV_AHEAD = 4, S_AHEAD = 4;
+    uint32_t vaddr[NVB], kaddr[NKB];
+    {
+        const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(smem);
+#pragma unroll
+        for (int db = 0; db < NVB; ++db) vaddr[db] = lds0 + vbase[db];
+#pragma unroll
+        for (int v = 0; v < NKB; ++v) kaddr[v] = lds0 + kbase[v];
+    }
 
     u32x4 qreg[D / 16];
     {
@@ -461,14 +521,35 @@ void attn_fwd16(Params p) {
         if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) return;
         f32x16 s[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            s[b] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const uint8_t *a = smem + KO + 32 * b * ROW_BYTES + kbase[ks % NKB] + 256 * (ks / NKB);
-                s[b] = Ty::mma(*(const u32x4 *)a, qreg[ks], s[b]);
-            }
+        for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+        {
+            // S^T = K Q^T: the NB chains interleaved, operand reads S_AHEAD
+            // products ahead of the matrix core
+            constexpr int NS = NB * (D / 16);
+            u32x4 ka[NS];
+            auto kread = [&](auto I_) {
+                constexpr int i = decltype(I_)::value, ks = i / NB, b = i % NB;
+                ka[i] = ds_read_b128_asm<KO + 32 * b * ROW_BYTES + 256 * (ks / NKB)>(kaddr[ks % NKB]);
+            };
+            static_for<0, (S_AHEAD < NS ? S_AHEAD : NS)>(kread);
+            static_for<0, NS>([&](auto I_) {
+                constexpr int i = decltype(I_)::value, ks = i / NB, b = i % NB;
+                if constexpr (i + S_AHEAD < NS) kread(std::integral_constant<int, i + S_AHEAD>{});
+                constexpr int later = (NS - 1 - i) < S_AHEAD ? (NS - 1 - i) : S_AHEAD;
+                lds_wait<later>(ka[i]);
+                s[b] = Ty::mma(ka[i], qreg[ks], s[b]);
+            });
         }
+        // first V^T operands of this tile, in flight under the softmax
+        constexpr int KSV = BK / 16, NPV = (D / 32) * KSV;
+        u32x2 ta[NPV], tb[NPV];
+        auto vread = [&](auto I_) {
+            constexpr int i = decltype(I_)::value, db = i / KSV, ks = i % KSV;
+            constexpr int off = VO + 16 * ks * ROW_BYTES + 256 * (db / NVB);
+            ta[i] = ds_read_tr16<off>(vaddr[db % NVB]);
+            tb[i] = ds_read_tr16<off + 8 * ROW_BYTES>(vaddr[db % NVB]);
+        };
+        static_for<0, (PV_AHEAD < NPV ? PV_AHEAD : NPV)>(vread);
         if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -484,7 +565,7 @@ void attn_fwd16(Params p) {
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
-        mt = max_halves(mt) * c;
+        mt = max_halves_swap(mt) * c;
         // move the reference max only when p could exceed 2^8 (exact either way)
         if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
             const float mnew = fmaxf(mref, mt);
@@ -509,404 +590,41 @@ void attn_fwd16(Params p) {
                     pb[2 * b + half][jj] = pk;
                     lsum = Ones::dot(pk, lsum, Ty{});
                 }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const uint8_t *a = smem + VO + 16 * ks * ROW_BYTES + vbase[db % NVB] + 256 * (db / NVB);
-                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a));
-                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_I16X4(a + 8 * ROW_BYTES));
-                const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
-                o[db] = Ty::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pb[ks], o[db]);
-            }
-        }
+        // O^T += V^T P^T: NPV products, their operand reads kept PV_AHEAD
+        // products ahead of the matrix core
+        static_for<0, NPV>([&](auto I_) {
+            constexpr int i = decltype(I_)::value, db = i / KSV, ks = i % KSV;
+            if constexpr (i + PV_AHEAD < NPV) vread(std::integral_constant<int, i + PV_AHEAD>{});
+            constexpr int later = (NPV - 1 - i) < PV_AHEAD ? (NPV - 1 - i) : PV_AHEAD;
+            lds_wait<2 * later>(ta[i], tb[i]);
+            o[db] = Ty::mma(u32x4{ta[i][0], ta[i][1], tb[i][0], tb[i][1]}, pb[ks], o[db]);
+        });
     };
 
     const int kb0 = w.kt_begin, ke = w.kt_end;
-    if constexpr (STAGES == 2) {
-        using B0K = std::integral_constant<int, 0>;
-        using B1K = std::integral_constant<int, TILE_BYTES>;
-        using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
-        using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
-        if (kb0 < ke) {
-            issue(kb0, B0K::value, B0V::value);
-            wait_vmem();
-            __syncthreads();
-            for (int kt = kb0; kt < ke; kt += 2) {
-                // tile kt in buffer 0 while tile kt+1 streams into buffer 1
-                if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
-                tile(B0K{}, B0V{}, kt);
-                wait_vmem();
-                __syncthreads();
-                if (kt + 1 >= ke) break;
-                // tile kt+1 in buffer 1 while tile kt+2 streams into buffer 0
-                if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
-                tile(B1K{}, B1V{}, kt + 1);
-                wait_vmem();
-                __syncthreads();
-            }
-        }
-    } else {
-        // three buffers: tile kt+2 streams in while kt is computed; at the end
-        // of tile kt only the batch of kt+1 must have landed (the newest batch,
-        // 2*LOADS loads of this wave, may stay in flight)
-        using K0 = std::integral_constant<int, 0>;
-        using K1 = std::integral_constant<int, TILE_BYTES>;
-        using K2 = std::integral_constant<int, 2 * TILE_BYTES>;
-        using V0 = std::integral_constant<int, 3 * TILE_BYTES>;
-        using V1 = std::integral_constant<int, 4 * TILE_BYTES>;
-        using V2 = std::integral_constant<int, 5 * TILE_BYTES>;
-        static_assert(2 * LOADS <= 15, "vmcnt field");
-        auto wait_next = [&](int kt) {
-            if (kt + 2 < ke) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS));   // vmcnt(2*LOADS)
-            else wait_vmem();
-            __syncthreads();
-        };
-        if (kb0 < ke) {
-            issue(kb0, K0::value, V0::value);
-            if (kb0 + 1 < ke) issue(kb0 + 1, K1::value, V1::value);
-            if (kb0 + 1 < ke) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS));
-            else wait_vmem();
-            __syncthreads();
-            for (int kt = kb0; kt < ke; kt += 3) {
-                if (kt + 2 < ke) issue(kt + 2, K2::value, V2::value);
-                tile(K0{}, V0{}, kt);
-                wait_next(kt);
-                if (kt + 1 >= ke) break;
-                if (kt + 3 < ke) issue(kt + 3, K0::value, V0::value);
-                tile(K1{}, V1{}, kt + 1);
-                wait_next(kt + 1);
-                if (kt + 2 >= ke) break;
-                if (kt + 4 < ke) issue(kt + 4, K1::value, V1::value);
-                tile(K2{}, V2{}, kt + 2);
-                wait_next(kt + 2);
-            }
-        }
-    }
-    write_rows<D>(p, w, r, g, o, mref, lsum);
-#endif
-}
-
-// ---- bf16 / fp16 kernel, two 32-row blocks per wavefront (head_dim <= 128) --------
-//
-// One wavefront per SIMD owns 64 rows as two 32-row blocks A and B that
-// share every K and V operand.  Each KV tile runs in four stages whose MFMA
-// and VALU work are independent, so the scheduler can interleave them in one
-// instruction stream and keep the matrix core busy while the softmax runs:
-//   1. S_A = K Q_A^T                      (MFMA)
-//   2. S_B = K Q_B^T  |  P_A = 2^(S_A c - m_A)   (MFMA | VALU)
-//   3. O_A += V^T P_A |  P_B = 2^(S_B c - m_B)   (MFMA | VALU)
-//   4. O_B += V^T P_B                     (MFMA)
-// The exponentials use the block's current reference max m without first
-// taking the tile's row max: a packed 16-bit max over P afterwards detects
-// the rare case where some p exceeds the type's bound (2^64 for bf16, 2^15 for
-// fp16; always on a row's first valid tile) and only then takes the row max,
-// rescales O and l and recomputes P.  Exact either way.
-
-constexpr int kRowsPerWave64 = 64;
-constexpr int kRowsPerGroup64 = kWaves * kRowsPerWave64;   // 256
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-template <class Ty> struct PBound;
-template <> struct PBound<Bf16> { [[maybe_unused]] static constexpr uint32_t bits = 0x5F80; };   // bf16 2^64
-template <> struct PBound<F16> { [[maybe_unused]] static constexpr uint32_t bits = 0x7800; };    // fp16 2^15
-
-// Scheduling pattern for one stage of the two-block kernel: `nm` MFMAs, each
-// followed by `nv` VALU instructions of the other block's softmax (the LDS
-// reads of the operands are left to the scheduler).
-template <int nm, int nv>
-__device__ inline void sched_stage() {
-#pragma unroll
-    for (int i = 0; i < nm; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
-    }
-}
-
-template <class Ty, int D, int BK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void attn_fwd16_w64(Params p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    static_assert(D % 32 == 0 && D <= 128 && BK % 32 == 0, "tile shape");
-    constexpr int CPR = D / 8;
-    constexpr int ROW_BYTES = CPR * 16;
-    constexpr int TILE_CHUNKS = BK * CPR;
-    constexpr int TILE_BYTES = TILE_CHUNKS * 16;
-    constexpr int LOADS = TILE_CHUNKS / (kWaves * kWave);
-    static_assert(LOADS * kWaves * kWave == TILE_CHUNKS, "staging split");
-    constexpr int NB = BK / 32;
-    constexpr int NKB = D / 16 < 8 ? D / 16 : 8;
-
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, g = lane >> 5;
-    const Tile w = locate<BK>(p);
-    const Rows rA = rows_of<kRowsPerWave64>(p, w, wave, l32);
-    const Rows rB = rows_of<kRowsPerWave64>(p, w, wave, 32 + l32);
-    const __amdgpu_buffer_rsrc_t rk =
-        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
-    const __amdgpu_buffer_rsrc_t rv =
-        head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES);
-
-    int koff[LOADS], voff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int pos = (wave * LOADS + i) * kWave + lane;
-        const int row = pos / CPR, cs = pos % CPR;
-        koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
-        voff[i] = pos * 16;
-    }
-    int kbase[NKB];
-#pragma unroll
-    for (int v = 0; v < NKB; ++v)
-        kbase[v] = l32 * ROW_BYTES + (((2 * v + g) ^ swz_k<CPR>(l32)) * 16);
-    const int vlane = lane * 16;
-
-    u32x4 qA[D / 16], qB[D / 16];
-    {
-        const uint16_t *pa = (const uint16_t *)p.q + (int64_t)(rA.ok ? rA.t : 0) * p.q_row_stride +
-                             (int64_t)rA.h * D + 8 * g;
-        const uint16_t *pb = (const uint16_t *)p.q + (int64_t)(rB.ok ? rB.t : 0) * p.q_row_stride +
-                             (int64_t)rB.h * D + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            qA[ks] = rA.ok ? *(const u32x4 *)(pa + 16 * ks) : u32x4{0, 0, 0, 0};
-            qB[ks] = rB.ok ? *(const u32x4 *)(pb + 16 * ks) : u32x4{0, 0, 0, 0};
-        }
-    }
-
-    f32x16 oA[D / 32], oB[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oA[db] = oB[db] = f32x16{};
-    float mA = -INFINITY, mB = -INFINITY;   // reference row max, log2 units
-    float lA = 0.f, lB = 0.f;               // this lane's share of the row sums
-    const float c = p.c;
-
-    auto issue = [&](int kt, int kdst, int vdst) {
-        const int base = kt * BK * D * 2;
-        const int vbase_t = (kt - p.vop_kt_lo) * TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
-        }
-    };
-    auto scores = [&](int KO, const u32x4 (&q)[D / 16], f32x16 (&s)[NB]) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            s[b] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const uint8_t *a = smem + KO + 32 * b * ROW_BYTES + kbase[ks % NKB] + 256 * (ks / NKB);
-                s[b] = Ty::mma(*(const u32x4 *)a, q[ks], s[b]);
-            }
-        }
-    };
-    auto apply_mask = [&](int j0, const Rows &r, f32x16 (&s)[NB]) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = j0 + 32 * b + (i / 4) * 8 + 4 * g + (i % 4);
-                if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
-            }
-    };
-    // P = 2^(s c - m) packed to the input type; returns the packed 16-bit max
-    // of P (both halves of the word) and the tile's row-sum share in lt
-    auto exps = [&](const f32x16 (&s)[NB], float m, u32x4 (&pk)[BK / 16], float &lt) -> uint32_t {
-        const float mc = m == -INFINITY ? 0.f : m;
-        u16x2 mx = {0, 0};
-        float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int i0 = 8 * half + 2 * jj;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
-                    const uint32_t w2 = Ty::pack(p0, p1);
-                    pk[2 * b + half][jj] = w2;
-                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w2));
-                    if (jj & 1) l1 = Ones::dot(w2, l1, Ty{});
-                    else l0 = Ones::dot(w2, l0, Ty{});
-                }
-        lt = l0 + l1;
-        return mx[0] > mx[1] ? mx[0] : mx[1];
-    };
-    // the rare path: move the reference max to the tile's row max, rescale
-    auto rescale_exps = [&](const f32x16 (&s)[NB], float &m, float &l, f32x16 (&o)[D / 32],
-                            u32x4 (&pk)[BK / 16], float &lt) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
-        mt = max_halves(mt) * c;
-        const float mnew = fmaxf(m, mt);
-        const float alpha = (mnew == -INFINITY || m == -INFINITY) ? (m == -INFINITY ? 0.f : 1.f)
-                                                                   : __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-        exps(s, m, pk, lt);
-    };
-    auto needs_rescale = [&](uint32_t pmax, float m) -> bool {
-        return m == -INFINITY ? pmax != 0 : pmax > PBound<Ty>::bits;
-    };
-    auto pv = [&](int VO, const u32x4 (&pk)[BK / 16], f32x16 (&o)[D / 32]) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 16) + ks) * 1024 + vlane);
-                o[db] = Ty::mma(a, pk[ks], o[db]);
-            }
-    };
-
-    // One 2-score chunk of a block's softmax: 2 FMA + 2 exp + pack + max + dot2.
-    // Chunk u covers registers i0 = 2*(u%8) of 32-key block u/8.
-    auto exp_chunk = [&](int u, const f32x16 (&s)[NB], float mc, u32x4 (&pk)[BK / 16],
-                         u16x2 &mx, float (&lt)[2]) {
-        const int b = u / 8, i0 = 2 * (u % 8);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
-        const uint32_t w2 = Ty::pack(p0, p1);
-        pk[2 * b + i0 / 8][(i0 % 8) / 2] = w2;
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w2));
-        lt[u & 1] = Ones::dot(w2, lt[u & 1], Ty{});
-    };
-    // K operand m of a scores stage: block m / (D/16), step m % (D/16)
-    auto kop = [&](int KO, int m) -> u32x4 {
-        const int b = m / (D / 16), ks = m % (D / 16);
-        return *(const u32x4 *)(smem + KO + 32 * b * ROW_BYTES + kbase[ks % NKB] + 256 * (ks / NKB));
-    };
-    // V operand m of a P.V stage: d block m / (BK/16), step m % (BK/16)
-    auto vop = [&](int VO, int m) -> u32x4 {
-        return *(const u32x4 *)(smem + VO + m * 1024 + vlane);
-    };
-    constexpr int NM = NB * (D / 16);          // MFMAs per stage (equal for S and P.V)
-    static_assert(NM == (D / 32) * (BK / 16), "stage sizes");
-    constexpr int NU = 8 * NB;                 // softmax chunks per block
-    constexpr int LEAD = 4;                    // LDS operands in flight
-
-    auto tile = [&](auto KO_, auto VO_, auto MASK_, int kt) {
-        constexpr int KO = decltype(KO_)::value, VO = decltype(VO_)::value;
-        constexpr bool MASK = decltype(MASK_)::value;
-        const int j0 = kt * BK;
-        f32x16 sA[NB], sB[NB];
-        u32x4 pA[BK / 16], pB[BK / 16];
-        u32x4 opnd[LEAD];
-        // 1: S_A
-#pragma unroll
-        for (int b = 0; b < NB; ++b) sA[b] = sB[b] = f32x16{};
-#pragma unroll
-        for (int m = 0; m < LEAD; ++m) opnd[m] = kop(KO, m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int b = m / (D / 16), ks = m % (D / 16);
-            sA[b] = Ty::mma(opnd[m % LEAD], qA[ks], sA[b]);
-            if (m + LEAD < NM) opnd[m % LEAD] = kop(KO, m + LEAD);
-        }
-        if (MASK) apply_mask(j0, rA, sA);
-        __builtin_amdgcn_sched_barrier(0);
-        // 2: S_B on the matrix core while block A's softmax runs on the VALU
-        const float mcA = mA == -INFINITY ? 0.f : mA;
-        u16x2 mxA = {0, 0};
-        float ltA[2] = {0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < LEAD; ++m) opnd[m] = kop(KO, m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int b = m / (D / 16), ks = m % (D / 16);
-            sB[b] = Ty::mma(opnd[m % LEAD], qB[ks], sB[b]);
-            if (m + LEAD < NM) opnd[m % LEAD] = kop(KO, m + LEAD);
-#pragma unroll
-            for (int u = m * NU / NM; u < (m + 1) * NU / NM; ++u) exp_chunk(u, sA, mcA, pA, mxA, ltA);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        {
-            float lt = ltA[0] + ltA[1];
-            const uint32_t pmax = mxA[0] > mxA[1] ? mxA[0] : mxA[1];
-            if (__builtin_amdgcn_ballot_w64(needs_rescale(pmax, mA)) != 0)
-                rescale_exps(sA, mA, lA, oA, pA, lt);
-            lA += lt;
-        }
-        if (MASK) apply_mask(j0, rB, sB);
-        __builtin_amdgcn_sched_barrier(0);
-        // 3: O_A += V^T P_A on the matrix core while block B's softmax runs
-        const float mcB = mB == -INFINITY ? 0.f : mB;
-        u16x2 mxB = {0, 0};
-        float ltB[2] = {0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < LEAD; ++m) opnd[m] = vop(VO, m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int db = m / (BK / 16), ks = m % (BK / 16);
-            oA[db] = Ty::mma(opnd[m % LEAD], pA[ks], oA[db]);
-            if (m + LEAD < NM) opnd[m % LEAD] = vop(VO, m + LEAD);
-#pragma unroll
-            for (int u = m * NU / NM; u < (m + 1) * NU / NM; ++u) exp_chunk(u, sB, mcB, pB, mxB, ltB);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        {
-            float lt = ltB[0] + ltB[1];
-            const uint32_t pmax = mxB[0] > mxB[1] ? mxB[0] : mxB[1];
-            if (__builtin_amdgcn_ballot_w64(needs_rescale(pmax, mB)) != 0)
-                rescale_exps(sB, mB, lB, oB, pB, lt);
-            lB += lt;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // 4: O_B += V^T P_B
-#pragma unroll
-        for (int m = 0; m < LEAD; ++m) opnd[m] = vop(VO, m);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const int db = m / (BK / 16), ks = m % (BK / 16);
-            oB[db] = Ty::mma(opnd[m % LEAD], pB[ks], oB[db]);
-            if (m + LEAD < NM) opnd[m % LEAD] = vop(VO, m + LEAD);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto step = [&](auto KO_, auto VO_, int kt) {
-        const int j0 = kt * BK;
-        if (!rA.wave_any || j0 > rA.w_pos_max || j0 + BK - 1 < rA.w_lo_min) return;
-        if (rA.wave_ragged || j0 < rA.w_lo_max || j0 + BK - 1 > rA.w_pos_min)
-            tile(KO_, VO_, std::true_type{}, kt);
-        else
-            tile(KO_, VO_, std::false_type{}, kt);
-    };
-
     using B0K = std::integral_constant<int, 0>;
     using B1K = std::integral_constant<int, TILE_BYTES>;
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
-    const int kb0 = w.kt_begin, ke = w.kt_end;
     if (kb0 < ke) {
         issue(kb0, B0K::value, B0V::value);
         wait_vmem();
         __syncthreads();
         for (int kt = kb0; kt < ke; kt += 2) {
+            // tile kt in buffer 0 while tile kt+1 streams into buffer 1
             if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
-            step(B0K{}, B0V{}, kt);
+            tile(B0K{}, B0V{}, kt);
             wait_vmem();
             __syncthreads();
             if (kt + 1 >= ke) break;
+            // tile kt+1 in buffer 1 while tile kt+2 streams into buffer 0
             if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
-            step(B1K{}, B1V{}, kt + 1);
+            tile(B1K{}, B1V{}, kt + 1);
             wait_vmem();
             __syncthreads();
         }
     }
-    write_rows<D>(p, w, rA, g, oA, mA, lA);
-    write_rows<D>(p, w, rB, g, oB, mB, lB);
+    write_rows<D>(p, w, r, g, o, mref, lsum);
 #endif
 }
 
@@ -1335,14 +1053,14 @@ struct Variant {
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 32, 64, 4, 2, 2>, nullptr},
-    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 64, 64, 4, 2, 2>, nullptr},
-    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 128, 64, 4, 2, 2>, nullptr},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
     {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64>, pack_v_operands<256, 64, true>},
     {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 32, 64, 4, 2, 2>, nullptr},
-    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 64, 64, 4, 2, 2>, nullptr},
-    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 128, 64, 4, 2, 2>, nullptr},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
     {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64>, pack_v_operands<256, 64, true>},
     {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32>, pack_v_operands<512, 32, true>},
     {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<32, 32>, nullptr},
