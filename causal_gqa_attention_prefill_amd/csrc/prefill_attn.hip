@@ -639,10 +639,15 @@ void attn_fwd16(Params p) {
 //   combine the four lane groups (l/16) with two exchanges;
 //   O^T block (16 d x 16 rows) += V^T P^T, k = 32 keys: P comes from two S^T
 //   blocks in the B-operand layout (slot (l/16, j): key 16*(j/4) + 4*(l/16) +
-//   j%4), V^T from two transposed LDS reads.
-// The V tile is swizzled for those reads: chunk c of row r sits at
+//   j%4).
+// V^T operands (VPACK false, head_dim 256): two transposed LDS reads of the
+// row-major V tile, which is swizzled for them: chunk c of row r sits at
 // c ^ (2 * (r % 8)), so the 8 rows x 32 bytes a half-wave reads per
-// transposed load fall in 16 different bank groups.
+// transposed load fall in 16 different bank groups.  VPACK true (head_dim
+// 512, where those reads bound the loop): the tiles come from the per-call
+// copy in operand order (pack_v_operands) and each operand is one
+// ds_read_b128; the copy costs a pass over the call's V rows, which only pays
+// off when each row is reused by many query tiles.
 
 constexpr int kWaves16 = 8;
 constexpr int kThreads16 = kWaves16 * kWave;
@@ -673,7 +678,7 @@ __device__ inline int swz_v16(int row) {
     return 2 * (row & 7);
 }
 
-template <class Ty, int D, int BK>
+template <class Ty, int D, int BK, bool VPACK>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -699,7 +704,8 @@ void attn_fwd16_r16(Params p) {
     const __amdgpu_buffer_rsrc_t rk =
         head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
     const __amdgpu_buffer_rsrc_t rv =
-        head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES);
+        VPACK ? head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES)
+              : head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
 
     int koff[LOADS], voff[LOADS];
 #pragma unroll
@@ -707,15 +713,31 @@ void attn_fwd16_r16(Params p) {
         const int pos = (wave * LOADS + i) * kWave + lane;
         const int row = pos / CPR, cs = pos % CPR;
         koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
-        voff[i] = pos * 16;                           // operand-ordered V: verbatim copy
+        voff[i] = VPACK ? pos * 16                    // operand-ordered V: verbatim copy
+                        : row * D * 2 + ((cs ^ swz_v16<CPR>(row)) * 16);
     }
     // K: chunk 4ks + g4 of row 16b + l16 sits at (4ks + g4) ^ l16: the XOR only
     // touches chunk bits 0-3, so step ks = 4u + v reads kbase[v] + 256u.
-    // V: operand (db, kp) of this lane is chunk (db * BK/32 + kp) * 64 + lane.
+    // V (VPACK): operand (db, kp) of this lane is chunk (db * BK/32 + kp) * 64 + lane.
+    // V (transposed reads): d-block db at key 0 is read at rows 4*g4 + l16/4,
+    // d = 16 db + 4 (lane%4); the XOR 2*(row%8) touches chunk bits 1-3, so
+    // block db = 8u + v reads vaddr[v] + 256u.  vaddr holds the address in
+    // the first V buffer; the buffer offset goes into the immediate.
     int kbase[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) kbase[v] = l16 * ROW_BYTES + (((4 * v + g4) ^ swz_k<CPR>(l16)) * 16);
     const int vlane = lane * 16;
+    constexpr int NVB16 = NDB < 8 ? NDB : 8;
+    uint32_t vaddr[VPACK ? 1 : NVB16];
+    if constexpr (!VPACK) {
+        const uint32_t v0 = (uint32_t)(uintptr_t)LDS_PTR(smem) + 2 * TILE_BYTES;
+        const int trow = 4 * g4 + l16 / 4;
+#pragma unroll
+        for (int v = 0; v < NVB16; ++v) {
+            const int d = 16 * v + 4 * (lane & 3);
+            vaddr[v] = v0 + trow * ROW_BYTES + (((d >> 3) ^ swz_v16<CPR>(trow)) * 16) + (d & 7) * 2;
+        }
+    }
 
     u32x4 qreg[NKS];
     {
@@ -734,7 +756,7 @@ void attn_fwd16_r16(Params p) {
 
     auto issue = [&](int kt, int kdst, int vdst) {
         const int base = kt * BK * D * 2;
-        const int vbase_t = (kt - p.vop_kt_lo) * TILE_BYTES;
+        const int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : base;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -795,13 +817,33 @@ void attn_fwd16_r16(Params p) {
                     pb[kp][2 * half + jj] = pk;
                     lsum = Ones::dot(pk, lsum, Ty{});
                 }
+        if constexpr (VPACK) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+            for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-            for (int kp = 0; kp < BK / 32; ++kp) {
-                const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 32) + kp) * 1024 + vlane);
-                o[db] = MM::mma(a, pb[kp], o[db]);
+                for (int kp = 0; kp < BK / 32; ++kp) {
+                    const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 32) + kp) * 1024 + vlane);
+                    o[db] = MM::mma(a, pb[kp], o[db]);
+                }
             }
+        } else {
+            // transposed reads, kept PV_AHEAD products ahead of the matrix core
+            constexpr int NPV = NDB * (BK / 32), PV_AHEAD = 4;
+            u32x2 ta[NPV], tb[NPV];
+            auto vread = [&](auto I_) {
+                constexpr int i = decltype(I_)::value, db = i / (BK / 32), kp = i % (BK / 32);
+                constexpr int off = VO - 2 * TILE_BYTES + 32 * kp * ROW_BYTES + 256 * (db / NVB16);
+                ta[i] = ds_read_tr16<off>(vaddr[db % NVB16]);
+                tb[i] = ds_read_tr16<off + 16 * ROW_BYTES>(vaddr[db % NVB16]);
+            };
+            static_for<0, (PV_AHEAD < NPV ? PV_AHEAD : NPV)>(vread);
+            static_for<0, NPV>([&](auto I_) {
+                constexpr int i = decltype(I_)::value, db = i / (BK / 32), kp = i % (BK / 32);
+                if constexpr (i + PV_AHEAD < NPV) vread(std::integral_constant<int, i + PV_AHEAD>{});
+                constexpr int later = (NPV - 1 - i) < PV_AHEAD ? (NPV - 1 - i) : PV_AHEAD;
+                lds_wait<2 * later>(ta[i], tb[i]);
+                o[db] = MM::mma(u32x4{ta[i][0], ta[i][1], tb[i][0], tb[i][1]}, pb[kp], o[db]);
+            });
         }
     };
 
@@ -830,19 +872,20 @@ void attn_fwd16_r16(Params p) {
     // the row's sum is spread over the four lane groups
     float ltot = lsum + __shfl_xor(lsum, 16);
     ltot = ltot + __shfl_xor(ltot, 32);
-    if (!r.ok) return;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float *dst;
-    if (p.S == 1) {
-        dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
-    } else {
-        const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
-        dst = p.ws_o + row * D + 4 * g4;
-        if (g4 == 0) p.ws_ml[row] = make_float2(mref, ltot);
-    }
+    if (r.ok) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        float *dst;
+        if (p.S == 1) {
+            dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+        } else {
+            const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
+            dst = p.ws_o + row * D + 4 * g4;
+            if (g4 == 0) p.ws_ml[row] = make_float2(mref, ltot);
+        }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-        *(f32x4 *)(dst + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+        for (int db = 0; db < NDB; ++db)
+            *(f32x4 *)(dst + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+    }
 #endif
 }
 
@@ -1041,7 +1084,6 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
 
 using KernelFn = void (*)(Params);
 using PackFn = void (*)(const uint16_t *, int64_t, int, int, int, uint16_t *);
-using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
 
 struct Variant {
     int dtype, D, BK;
@@ -1056,18 +1098,20 @@ const Variant kVariants[] = {
     {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
     {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
     {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64>, pack_v_operands<256, 64, true>},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64, false>, nullptr},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32, true>, pack_v_operands<512, 32, true>},
     {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
     {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
     {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64>, pack_v_operands<256, 64, true>},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64, false>, nullptr},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32, true>, pack_v_operands<512, 32, true>},
     {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<32, 32>, nullptr},
     {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<64, 32>, nullptr},
     {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<128, 32>, nullptr},
     {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, attn_fwd32<256, 32>, nullptr},
 };
+
+using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
 
 MergeFn merge_for(int D) {
     switch (D) {
