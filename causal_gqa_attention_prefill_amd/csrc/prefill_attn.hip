@@ -324,6 +324,20 @@ __device__ inline void lds_wait(u32x4 &a) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Maximum over lanes l and l ^ 16 (the 16-lane rows of each half), likewise
+// without LDS: the row swap leaves x[l] and x[l ^ 16] in the two results.
+[[maybe_unused]] __device__ inline float max_quarters_swap(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max(a, b, c) as one v_max3_f32: written as fmaxf the compiler rebalances a
+// row-max chain into two-operand maxima (0.75 instead of 0.5 instructions per
+// score).  Scores are finite or -inf here.
+[[maybe_unused]] __device__ inline float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 template <int I, int N, class F>
 __device__ inline void static_for(F &&f) {
     if constexpr (I < N) {
@@ -559,13 +573,17 @@ void attn_fwd16(Params p) {
                     if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
                 }
         }
-        // row max of the tile (raw scores), both lane halves
-        float mt = -INFINITY;
+        // row max of the tile (raw scores), both lane halves; two independent
+        // v_max3 chains so that no instruction waits on the one before it
+        float mt0 = -INFINITY, mt1 = -INFINITY;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[b][i], s[b][i + 1]));
-        mt = max_halves_swap(mt) * c;
+            for (int i = 0; i < 16; i += 4) {
+                mt0 = max3(mt0, s[b][i], s[b][i + 1]);
+                mt1 = max3(mt1, s[b][i + 2], s[b][i + 3]);
+            }
+        float mt = max_halves_swap(fmaxf(mt0, mt1)) * c;
         // move the reference max only when p could exceed 2^8 (exact either way)
         if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
             const float mnew = fmaxf(mref, mt);
@@ -789,11 +807,13 @@ void attn_fwd16_r16(Params p) {
                     if (key < r.lo || key > r.pos) s[b][i] = -INFINITY;
                 }
         }
-        float mt = -INFINITY;
+        float mt0 = -INFINITY, mt1 = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < NSB; ++b) mt = fmaxf(mt, fmaxf(fmaxf(s[b][0], s[b][1]), fmaxf(s[b][2], s[b][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+        for (int b = 0; b < NSB; ++b) {
+            mt0 = max3(mt0, s[b][0], s[b][1]);
+            mt1 = max3(mt1, s[b][2], s[b][3]);
+        }
+        const float mt = max_halves_swap(max_quarters_swap(fmaxf(mt0, mt1))) * c;
         if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
             const float mnew = fmaxf(mref, mt);
             const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
