@@ -696,29 +696,35 @@ __device__ inline int swz_v16(int row) {
     return 2 * (row & 7);
 }
 
-template <class Ty, int D, int BK, bool VPACK>
+template <class Ty, int D, int BK, bool VPACK, int KSPLIT>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(D >= 128 && D % 32 == 0 && BK % 32 == 0, "tile shape");
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && !VPACK), "key halves read V in place");
+    constexpr int NWH = kWaves16 / KSPLIT;            // wavefronts per key half
     using MM = typename M16<Ty>::T;
     constexpr int CPR = D / 8;
     constexpr int ROW_BYTES = CPR * 16;
     constexpr int TILE_CHUNKS = BK * CPR;
     constexpr int TILE_BYTES = TILE_CHUNKS * 16;
-    constexpr int LOADS = TILE_CHUNKS / (kWaves16 * kWave);
-    static_assert(LOADS * kWaves16 * kWave == TILE_CHUNKS, "staging split");
+    constexpr int LOADS = TILE_CHUNKS / (NWH * kWave);
+    static_assert(LOADS * NWH * kWave == TILE_CHUNKS, "staging split");
     constexpr int NKS = D / 32;                       // k steps of S
     constexpr int NDB = D / 16;                       // 16-wide d blocks of O
     constexpr int NSB = BK / 16;                      // 16-key blocks of S per tile
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE_BYTES];
+    // per key half: [K buffer 0, K buffer 1, V buffer 0, V buffer 1]
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KSPLIT * 4 * TILE_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = KSPLIT == 1 ? 0 : wave / NWH;    // key half
+    const int hw = KSPLIT == 1 ? wave : wave % NWH;   // wavefront within it
+    uint8_t *const sm = KSPLIT == 1 ? smem : smem + half * 4 * TILE_BYTES;
     const int l16 = lane & 15, g4 = lane >> 4;
     const Tile w = locate<BK>(p);
-    const Rows r = rows_of<kRowsPerWave16>(p, w, wave, l16);
+    const Rows r = rows_of<kRowsPerWave16>(p, w, hw, l16);
     const __amdgpu_buffer_rsrc_t rk =
         head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
     const __amdgpu_buffer_rsrc_t rv =
@@ -728,7 +734,7 @@ void attn_fwd16_r16(Params p) {
     int koff[LOADS], voff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-        const int pos = (wave * LOADS + i) * kWave + lane;
+        const int pos = (hw * LOADS + i) * kWave + lane;
         const int row = pos / CPR, cs = pos % CPR;
         koff[i] = row * D * 2 + ((cs ^ swz_k<CPR>(row)) * 16);
         voff[i] = VPACK ? pos * 16                    // operand-ordered V: verbatim copy
@@ -748,7 +754,7 @@ void attn_fwd16_r16(Params p) {
     constexpr int NVB16 = NDB < 8 ? NDB : 8;
     uint32_t vaddr[VPACK ? 1 : NVB16];
     if constexpr (!VPACK) {
-        const uint32_t v0 = (uint32_t)(uintptr_t)LDS_PTR(smem) + 2 * TILE_BYTES;
+        const uint32_t v0 = (uint32_t)(uintptr_t)LDS_PTR(sm) + 2 * TILE_BYTES;
         const int trow = 4 * g4 + l16 / 4;
 #pragma unroll
         for (int v = 0; v < NVB16; ++v) {
@@ -778,9 +784,9 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+                rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
+                rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
         }
     };
 
@@ -794,7 +800,7 @@ void attn_fwd16_r16(Params p) {
             s[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const uint8_t *a = smem + KO + 16 * b * ROW_BYTES + kbase[ks % 4] + 256 * (ks / 4);
+                const uint8_t *a = sm + KO + 16 * b * ROW_BYTES + kbase[ks % 4] + 256 * (ks / 4);
                 s[b] = MM::mma(*(const u32x4 *)a, qreg[ks], s[b]);
             }
         }
@@ -842,7 +848,7 @@ void attn_fwd16_r16(Params p) {
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int kp = 0; kp < BK / 32; ++kp) {
-                    const u32x4 a = *(const u32x4 *)(smem + VO + (db * (BK / 32) + kp) * 1024 + vlane);
+                    const u32x4 a = *(const u32x4 *)(sm + VO + (db * (BK / 32) + kp) * 1024 + vlane);
                     o[db] = MM::mma(a, pb[kp], o[db]);
                 }
             }
@@ -872,27 +878,83 @@ void attn_fwd16_r16(Params p) {
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
     const int kb0 = w.kt_begin, ke = w.kt_end;
-    if (kb0 < ke) {
-        issue(kb0, B0K::value, B0V::value);
-        wait_vmem();
+    if constexpr (KSPLIT == 1) {
+        if (kb0 < ke) {
+            issue(kb0, B0K::value, B0V::value);
+            wait_vmem();
+            __syncthreads();
+            for (int kt = kb0; kt < ke; kt += 2) {
+                if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
+                tile(B0K{}, B0V{}, kt);
+                wait_vmem();
+                __syncthreads();
+                if (kt + 1 >= ke) break;
+                if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
+                tile(B1K{}, B1V{}, kt + 1);
+                wait_vmem();
+                __syncthreads();
+            }
+        }
+    } else {
+        // the first half takes the first ceil(n/2) of the work-group's n KV
+        // tiles, the second half the rest; both step through the same number
+        // of iterations so that they share every barrier
+        const int niter = (ke - kb0 + 1) / 2;
+        const int hb = half == 1 ? kb0 + niter : kb0;
+        const int he = half == 0 ? kb0 + niter : ke;
+        if (niter > 0) {
+            if (hb < he) issue(hb, B0K::value, B0V::value);
+            wait_vmem();
+            __syncthreads();
+            for (int it = 0; it < niter; it += 2) {
+                const int kt = hb + it;
+                if (kt + 1 < he) issue(kt + 1, B1K::value, B1V::value);
+                if (kt < he) tile(B0K{}, B0V{}, kt);
+                wait_vmem();
+                __syncthreads();
+                if (it + 1 >= niter) break;
+                if (kt + 2 < he) issue(kt + 2, B0K::value, B0V::value);
+                if (kt + 1 < he) tile(B1K{}, B1V{}, kt + 1);
+                wait_vmem();
+                __syncthreads();
+            }
+        }
+    }
+
+    if constexpr (KSPLIT == 2) {
+        // the second half hands (O, m, l) of its rows to the wavefront of the
+        // first half that holds the same rows (same hw and lane); the buffers
+        // are free after the loop's last barrier
+        constexpr int NX = NDB * 4 + 2;
+        static_assert(NWH * NX * kWave * 4 <= KSPLIT * 4 * TILE_BYTES, "exchange fits in LDS");
+        float *xch = (float *)smem + hw * NX * kWave + lane;
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xch[(4 * db + i) * kWave] = o[db][i];
+            xch[(NX - 2) * kWave] = mref;
+            xch[(NX - 1) * kWave] = lsum;
+        }
         __syncthreads();
-        for (int kt = kb0; kt < ke; kt += 2) {
-            if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
-            tile(B0K{}, B0V{}, kt);
-            wait_vmem();
-            __syncthreads();
-            if (kt + 1 >= ke) break;
-            if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
-            tile(B1K{}, B1V{}, kt + 1);
-            wait_vmem();
-            __syncthreads();
+        if (half == 0) {
+            const float m1 = xch[(NX - 2) * kWave], l1 = xch[(NX - 1) * kWave];
+            const float ms = fmaxf(mref, m1);
+            const float a0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - ms);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - ms);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a0 + xch[(4 * db + i) * kWave] * a1;
+            lsum = lsum * a0 + l1 * a1;
+            mref = ms;
         }
     }
 
     // the row's sum is spread over the four lane groups
     float ltot = lsum + __shfl_xor(lsum, 16);
     ltot = ltot + __shfl_xor(ltot, 32);
-    if (r.ok) {
+    if (r.ok && (KSPLIT == 1 || half == 0)) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         float *dst;
         if (p.S == 1) {
@@ -1118,13 +1180,15 @@ const Variant kVariants[] = {
     {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
     {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
     {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64, false>, nullptr},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32, true>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64, false, 1>, nullptr},
+    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, attn_fwd16_r16<Bf16, 256, 32, false, 2>, nullptr},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
     {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
     {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
     {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64, false>, nullptr},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32, true>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64, false, 1>, nullptr},
+    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, attn_fwd16_r16<F16, 256, 32, false, 2>, nullptr},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
     {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<32, 32>, nullptr},
     {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<64, 32>, nullptr},
     {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<128, 32>, nullptr},
@@ -1147,6 +1211,15 @@ MergeFn merge_for(int D) {
 const Variant *find_variant(int dtype, int D) {
     for (const Variant &v : kVariants)
         if (v.dtype == dtype && v.D == D) return &v;
+    return nullptr;
+}
+
+// The variant whose work-groups split each tile's keys between two halves of
+// their wavefronts (half the rows per work-group), if this dtype and
+// head_dim have one.
+const Variant *find_half_rows_variant(int dtype, int D) {
+    for (const Variant &v : kVariants)
+        if (v.dtype == dtype && v.D == D && v.rows < kRowsPerGroup) return &v;
     return nullptr;
 }
 
@@ -1219,6 +1292,13 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st != PA_OK) return st;
     const Variant *var = find_variant(dtype, D);
+    // When full-size tiles cannot occupy every CU, work-groups that split each
+    // tile's keys between their two wavefront halves (merged in LDS) come
+    // before splitting the keys across work-groups (merged by a separate pass).
+    if (const Variant *alt = find_half_rows_variant(dtype, D)) {
+        const int64_t base = cdiv(T, var->rows / (H / KVH)) * KVH;
+        if (base < (int64_t)kCus * var->groups_per_cu && alt->rows >= H / KVH) var = alt;
+    }
     pl->var = var;
     pl->G = H / KVH;
     pl->TQ = var->rows / pl->G;
