@@ -87,6 +87,7 @@ struct Params {
     int S;            // key splits per tile
     int n_items;      // nq * KVH * S work-groups
     float c;          // log2(e) / sqrt(head_dim)
+    int order;        // 1: within a die, longest query tiles first then shortest first; 0: longest first
     int kv_bytes;     // bytes of the L valid rows of one kv head (16-bit kernels)
     const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
     int vop_kt_lo;         // first KV tile held in vop
@@ -145,11 +146,13 @@ __device__ inline Tile locate(const Params &p) {
     const int rest = item / p.nq;
     w.split = rest % p.S;
     w.kvh = rest / p.S;
-    // The first half of a die's range runs the longest rows first and the
-    // second half the shortest first, so the two work-groups a CU receives
-    // when the range is dealt round-robin over its CUs carry similar work.
+    // order 1 (two resident work-groups per CU): the first half of a die's
+    // range runs the longest rows first and the second half the shortest
+    // first, so the two work-groups a CU receives when the range is dealt
+    // round-robin over its CUs carry similar work.  order 0 (one per CU):
+    // longest first, so that the dispatcher's refills balance the tail.
     const int half_ = (p.nq + 1) / 2;
-    const int qtile = qi < half_ ? p.nq - 1 - qi : qi - half_;
+    const int qtile = p.order == 0 ? p.nq - 1 - qi : qi < half_ ? p.nq - 1 - qi : qi - half_;
     w.t0 = qtile * p.TQ;
     w.t_last = min(w.t0 + p.TQ, p.T) - 1;
     const int lo = first_key(p.start_pos + w.t0, p.window);
@@ -1172,27 +1175,28 @@ struct Variant {
     int groups_per_cu;         // resident work-groups per CU the kernel is sized for
     int threads;               // work-group size (4 or 8 wavefronts)
     int rows;                  // (token, head) rows per work-group
+    int ksplit;                // 2: the tile's keys are split between two wavefront halves
     KernelFn fn;
     PackFn pack;               // V operand-order pass (16-bit inputs), else null
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 256, 64, false, 1>, nullptr},
-    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, attn_fwd16_r16<Bf16, 256, 32, false, 2>, nullptr},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<Bf16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 256, 64, false, 1>, nullptr},
-    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, attn_fwd16_r16<F16, 256, 32, false, 2>, nullptr},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, attn_fwd16_r16<F16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<32, 32>, nullptr},
-    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<64, 32>, nullptr},
-    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, attn_fwd32<128, 32>, nullptr},
-    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, attn_fwd32<256, 32>, nullptr},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1>, nullptr},
+    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2>, nullptr},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1>, nullptr},
+    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2>, nullptr},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<32, 32>, nullptr},
+    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<64, 32>, nullptr},
+    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<128, 32>, nullptr},
+    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, nullptr},
 };
 
 using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
@@ -1210,16 +1214,15 @@ MergeFn merge_for(int D) {
 
 const Variant *find_variant(int dtype, int D) {
     for (const Variant &v : kVariants)
-        if (v.dtype == dtype && v.D == D) return &v;
+        if (v.dtype == dtype && v.D == D && v.ksplit == 1) return &v;
     return nullptr;
 }
 
 // The variant whose work-groups split each tile's keys between two halves of
-// their wavefronts (half the rows per work-group), if this dtype and
-// head_dim have one.
-const Variant *find_half_rows_variant(int dtype, int D) {
+// their wavefronts, if this dtype and head_dim have one.
+const Variant *find_ksplit_variant(int dtype, int D) {
     for (const Variant &v : kVariants)
-        if (v.dtype == dtype && v.D == D && v.rows < kRowsPerGroup) return &v;
+        if (v.dtype == dtype && v.D == D && v.ksplit == 2) return &v;
     return nullptr;
 }
 
@@ -1295,7 +1298,7 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     // When full-size tiles cannot occupy every CU, work-groups that split each
     // tile's keys between their two wavefront halves (merged in LDS) come
     // before splitting the keys across work-groups (merged by a separate pass).
-    if (const Variant *alt = find_half_rows_variant(dtype, D)) {
+    if (const Variant *alt = find_ksplit_variant(dtype, D)) {
         const int64_t base = cdiv(T, var->rows / (H / KVH)) * KVH;
         if (base < (int64_t)kCus * var->groups_per_cu && alt->rows >= H / KVH) var = alt;
     }
@@ -1366,6 +1369,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.S = pl.S;
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
+    p.order = pl.var->groups_per_cu == 2 ? 1 : 0;
     p.kv_bytes = (int)std::min<int64_t>(((int64_t)start_pos + T) * D * elem_bytes(dtype), INT32_MAX);
     if (pl.var->pack) {
         hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream,
