@@ -142,25 +142,46 @@ def prefill_attn(q, k_cache, v_cache, out, T, start_pos, num_heads, num_kv_heads
     return out
 
 
+class PreparedCall:
+    """prefill_attn_ex with its arguments checked and marshalled once.
+
+    For callers that launch the same call repeatedly (a chunk loop, a
+    benchmark): calling the object issues just the C-ABI call.  The tensors
+    are kept referenced; their storage must not be reallocated meanwhile.
+    """
+
+    def __init__(self, q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
+                 start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
+                 stream=None):
+        dt = _dtype_of(q)
+        if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+            raise TypeError("q, k_cache and v_cache must share one storage type")
+        L = start_pos + T
+        _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
+        _need(k_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "k_cache")
+        _need(v_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "v_cache")
+        _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        self._fn = load().prefill_attn_ex
+        self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                      v_cache.data_ptr(), kv_head_stride, out.data_ptr(), out_row_stride, T,
+                      start_pos, num_heads, num_kv_heads, head_dim, window, ws_ptr, ws_bytes,
+                      _stream(stream))
+        self._keep = (q, k_cache, v_cache, out, workspace)
+        self.out = out
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            raise PrefillAttnError(st, "prefill_attn_ex")
+        return self.out
+
+
 def prefill_attn_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                     start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
                     stream=None):
     """Strided call; workspace is a device tensor (any dtype) or None."""
-    dt = _dtype_of(q)
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise TypeError("q, k_cache and v_cache must share one storage type")
-    L = start_pos + T
-    _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
-    _need(k_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "k_cache")
-    _need(v_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "v_cache")
-    _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    st = load().prefill_attn_ex(DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
-                                v_cache.data_ptr(), kv_head_stride, out.data_ptr(), out_row_stride,
-                                T, start_pos, num_heads, num_kv_heads, head_dim, window, ws_ptr,
-                                ws_bytes, _stream(stream))
-    if st != PA_OK:
-        raise PrefillAttnError(st, "prefill_attn_ex")
-    return out
+    return PreparedCall(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
+                        start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream)()
