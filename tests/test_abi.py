@@ -106,3 +106,15 @@ def test_binding_has_no_cpu_path():
     src = open(binding.__file__).read()
     assert "oracle" not in src.replace("no fallback", "")
     assert "numpy" not in src
+
+
+def test_prepared_call_rejects_host_tensors():
+    # the prepared form checks its arguments like prefill_attn_ex: host tensors are refused
+    import torch
+    q = torch.zeros(4, 2 * 32, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 4, 32, dtype=torch.bfloat16)
+    out = torch.zeros(4, 2 * 32, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        pa.PreparedCall(q, 64, kv, kv, 4 * 32, out, 64, 4, 0, 2, 1, 32)
+    with pytest.raises(ValueError):
+        pa.prefill_attn_ex(q, 64, kv, kv, 4 * 32, out, 64, 4, 0, 2, 1, 32)
