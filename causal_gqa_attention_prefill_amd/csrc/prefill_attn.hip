@@ -754,6 +754,12 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) kbase[v] = l16 * ROW_BYTES + (((4 * v + g4) ^ swz_k<CPR>(l16)) * 16);
     const int vlane = lane * 16;
+    uint32_t kaddr[4];
+    {
+        const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(sm);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) kaddr[v] = lds0 + kbase[v];
+    }
     constexpr int NVB16 = NDB < 8 ? NDB : 8;
     uint32_t vaddr[VPACK ? 1 : NVB16];
     if constexpr (!VPACK) {
@@ -797,15 +803,27 @@ void attn_fwd16_r16(Params p) {
         constexpr int KO = decltype(KO_)::value, VO = decltype(VO_)::value;
         const int j0 = kt * BK;
         if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) return;
+        // S^T = K Q^T: the NSB chains interleaved, operand reads S_AHEAD
+        // products ahead (16x16x32 products are short, so reads run further
+        // ahead than in the 32-row kernel)
         f32x4v s[NSB];
 #pragma unroll
-        for (int b = 0; b < NSB; ++b) {
-            s[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const uint8_t *a = sm + KO + 16 * b * ROW_BYTES + kbase[ks % 4] + 256 * (ks / 4);
-                s[b] = MM::mma(*(const u32x4 *)a, qreg[ks], s[b]);
-            }
+        for (int b = 0; b < NSB; ++b) s[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int NS = NSB * NKS, S_AHEAD = 6;
+            u32x4 ka[NS];
+            auto kread = [&](auto I_) {
+                constexpr int i = decltype(I_)::value, ks = i / NSB, b = i % NSB;
+                ka[i] = ds_read_b128_asm<KO + 16 * b * ROW_BYTES + 256 * (ks / 4)>(kaddr[ks % 4]);
+            };
+            static_for<0, (S_AHEAD < NS ? S_AHEAD : NS)>(kread);
+            static_for<0, NS>([&](auto I_) {
+                constexpr int i = decltype(I_)::value, ks = i / NSB, b = i % NSB;
+                if constexpr (i + S_AHEAD < NS) kread(std::integral_constant<int, i + S_AHEAD>{});
+                constexpr int later = (NS - 1 - i) < S_AHEAD ? (NS - 1 - i) : S_AHEAD;
+                lds_wait<later>(ka[i]);
+                s[b] = MM::mma(ka[i], qreg[ks], s[b]);
+            });
         }
         if (r.wave_ragged || j0 < r.w_lo_max || j0 + BK - 1 > r.w_pos_min) {
 #pragma unroll
@@ -857,7 +875,7 @@ void attn_fwd16_r16(Params p) {
             }
         } else {
             // transposed reads, kept PV_AHEAD products ahead of the matrix core
-            constexpr int NPV = NDB * (BK / 32), PV_AHEAD = 4;
+            constexpr int NPV = NDB * (BK / 32), PV_AHEAD = 7;   // 14 reads in flight
             u32x2 ta[NPV], tb[NPV];
             auto vread = [&](auto I_) {
                 constexpr int i = decltype(I_)::value, db = i / (BK / 32), kp = i % (BK / 32);
