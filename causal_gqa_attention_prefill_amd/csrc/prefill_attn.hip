@@ -762,7 +762,9 @@ void attn_fwd16_r16(Params p) {
     }
     constexpr int NVB16 = NDB < 8 ? NDB : 8;
     uint32_t vaddr[VPACK ? 1 : NVB16];
-    if constexpr (!VPACK) {
+    if constexpr (VPACK) {
+        vaddr[0] = (uint32_t)(uintptr_t)LDS_PTR(sm) + 2 * TILE_BYTES + vlane;
+    } else {
         const uint32_t v0 = (uint32_t)(uintptr_t)LDS_PTR(sm) + 2 * TILE_BYTES;
         const int trow = 4 * g4 + l16 / 4;
 #pragma unroll
@@ -865,14 +867,22 @@ void attn_fwd16_r16(Params p) {
                     lsum = Ones::dot(pk, lsum, Ty{});
                 }
         if constexpr (VPACK) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int kp = 0; kp < BK / 32; ++kp) {
-                    const u32x4 a = *(const u32x4 *)(sm + VO + (db * (BK / 32) + kp) * 1024 + vlane);
-                    o[db] = MM::mma(a, pb[kp], o[db]);
-                }
-            }
+            // operand-ordered V: one ds_read_b128 per product, PV_AHEAD ahead;
+            // vaddr[0] addresses the first V buffer, the rest is immediate
+            constexpr int NPV = NDB * (BK / 32), PV_AHEAD = 6;
+            u32x4 va[NPV];
+            auto vread = [&](auto I_) {
+                constexpr int i = decltype(I_)::value;
+                va[i] = ds_read_b128_asm<VO - 2 * TILE_BYTES + i * 1024>(vaddr[0]);
+            };
+            static_for<0, (PV_AHEAD < NPV ? PV_AHEAD : NPV)>(vread);
+            static_for<0, NPV>([&](auto I_) {
+                constexpr int i = decltype(I_)::value, db = i / (BK / 32), kp = i % (BK / 32);
+                if constexpr (i + PV_AHEAD < NPV) vread(std::integral_constant<int, i + PV_AHEAD>{});
+                constexpr int later = (NPV - 1 - i) < PV_AHEAD ? (NPV - 1 - i) : PV_AHEAD;
+                lds_wait<later>(va[i]);
+                o[db] = MM::mma(va[i], pb[kp], o[db]);
+            });
         } else {
             // transposed reads, kept PV_AHEAD products ahead of the matrix core
             constexpr int NPV = NDB * (BK / 32), PV_AHEAD = 7;   // 14 reads in flight
