@@ -12,7 +12,9 @@ call.  The ``roofline`` object prices the fused kernel against the dense bf16
 MFMA peak, with the average launch time taken from HIP events on the launch
 stream around the timed steps; ``cpu_baseline`` times the fp64 oracle on a
 bounded sample of the same workload on the host cores.  Diagnostics (per-call
-events over a few extra steps) go to stderr.
+events over a few extra steps) go to stderr.  Unless --warmup is given, the
+untimed warm-up lasts at least WARMUP_S seconds, long enough for the GPU to
+reach its working clock; the JSON line reports the number of warm-up steps.
 """
 from __future__ import annotations
 
@@ -34,6 +36,7 @@ import workloads  # noqa: E402
 METRIC = "prefill attention TFLOP/s and % of MI355X bf16 MFMA peak (T=2048 chunk)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_GBS = 8000.0
+WARMUP_S = 0.3
 KERNEL_SOURCE = os.path.join(ROOT, "causal_gqa_attention_prefill_amd", "csrc", "prefill_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -128,8 +131,10 @@ def calibrate_copy(nbytes: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 10 steps and "
+                         f"{WARMUP_S} s of work, so that the GPU has left its idle clocks)")
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -190,8 +195,20 @@ def main():
             if events is not None:
                 events[i][1].record()
 
-    for _ in range(args.warmup):
-        step()
+    # warm-up: from idle the GPU needs some tens of ms of load to reach its
+    # working clock (measured: the first 25 steps of the default workload run
+    # ~15% slower than steady state), so by default warm up by time
+    if args.warmup is None:
+        n_warm, t_w = 0, time.perf_counter()
+        while n_warm < 10 or time.perf_counter() - t_w < WARMUP_S:
+            for _ in range(10):
+                step()
+            n_warm += 10
+            torch.cuda.synchronize()
+        args.warmup = n_warm
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
 
     # timed region: K steps back to back, wall clock for the job throughput and

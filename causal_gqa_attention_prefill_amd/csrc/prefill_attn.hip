@@ -209,6 +209,8 @@ __device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r,
     if (!r.ok) return;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (p.S == 1) {
+        // written once and not read again by this call: non-temporal stores keep
+        // the output from displacing cached K/V lines
         float *dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -216,7 +218,7 @@ __device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r,
             for (int r4 = 0; r4 < 4; ++r4) {
                 f32x4 val = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv,
                              o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
-                *(f32x4 *)(dst + 32 * db + 8 * r4) = val;
+                __builtin_nontemporal_store(val, (f32x4 *)(dst + 32 * db + 8 * r4));
             }
     } else {
         const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
@@ -987,17 +989,21 @@ void attn_fwd16_r16(Params p) {
     ltot = ltot + __shfl_xor(ltot, 32);
     if (r.ok && (KSPLIT == 1 || half == 0)) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        float *dst;
         if (p.S == 1) {
-            dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+            float *dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                __builtin_nontemporal_store(
+                    f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv},
+                    (f32x4 *)(dst + 16 * db));
         } else {
             const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
-            dst = p.ws_o + row * D + 4 * g4;
+            float *dst = p.ws_o + row * D + 4 * g4;
             if (g4 == 0) p.ws_ml[row] = make_float2(mref, ltot);
-        }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-            *(f32x4 *)(dst + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+            for (int db = 0; db < NDB; ++db)
+                *(f32x4 *)(dst + 16 * db) = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+        }
     }
 #endif
 }
@@ -1190,7 +1196,8 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
         }
     }
     const int t = (int)(row / H), h = (int)(row % H);
-    *(f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4) = acc * (1.f / wsum);
+    __builtin_nontemporal_store(acc * (1.f / wsum),
+                                (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
 }
 
 // ---- host side -----------------------------------------------------------------------
