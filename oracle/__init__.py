@@ -84,48 +84,63 @@ class Oracle:
             _FP, _I64, _FP, _FP, _I64, _INT, _INT, _DP, ctypes.POINTER(_INT),
             _INT, _INT, _INT, _INT, _INT, _INT]
         lib.oracle_row_probabilities.restype = _INT
+        lib.oracle_prefill_attention_ring.argtypes = [
+            _FP, _I64, _FP, _FP, _I64, _INT, _DP, _INT, _INT, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_prefill_attention_ring.restype = _INT
+        lib.oracle_prefill_attention_rows_ring.argtypes = [
+            _FP, _I64, _FP, _FP, _I64, _INT, _IP, _IP, _I64, _DP,
+            _INT, _INT, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_prefill_attention_rows_ring.restype = _INT
         self.lib = lib
 
     @staticmethod
-    def _strides(q, k, T, start_pos, num_heads, head_dim, q_row_stride, kv_head_stride):
+    def _strides(q, k, T, start_pos, num_heads, head_dim, q_row_stride, kv_head_stride,
+                 ring_slots=0):
         if q_row_stride is None:
             q_row_stride = num_heads * head_dim
         if kv_head_stride is None:
-            kv_head_stride = (start_pos + T) * head_dim
+            kv_head_stride = (ring_slots or (start_pos + T)) * head_dim
         return int(q_row_stride), int(kv_head_stride)
 
     def attention(self, q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim,
-                  window=0, q_row_stride=None, kv_head_stride=None, nthreads=None):
-        """Whole chunk; returns fp64 [T, num_heads, head_dim]."""
+                  window=0, q_row_stride=None, kv_head_stride=None, nthreads=None, ring_slots=0):
+        """Whole chunk; returns fp64 [T, num_heads, head_dim].  ring_slots > 0:
+        k and v are ring caches, key j in slot j % ring_slots."""
         q, k, v = _f32(q), _f32(k), _f32(v)
         qs, ks = self._strides(q, k, T, start_pos, num_heads, head_dim,
-                               q_row_stride, kv_head_stride)
-        _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks)
+                               q_row_stride, kv_head_stride, ring_slots)
+        _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks, ring_slots)
         out = np.empty((T, num_heads, head_dim), dtype=np.float64)
-        rc = self.lib.oracle_prefill_attention(
-            _ptr(q, _FP), qs, _ptr(k, _FP), _ptr(v, _FP), ks, _ptr(out, _DP),
-            T, start_pos, num_heads, num_kv_heads, head_dim, window,
-            nthreads or default_threads())
+        if ring_slots:
+            rc = self.lib.oracle_prefill_attention_ring(
+                _ptr(q, _FP), qs, _ptr(k, _FP), _ptr(v, _FP), ks, int(ring_slots), _ptr(out, _DP),
+                T, start_pos, num_heads, num_kv_heads, head_dim, window,
+                nthreads or default_threads())
+        else:
+            rc = self.lib.oracle_prefill_attention(
+                _ptr(q, _FP), qs, _ptr(k, _FP), _ptr(v, _FP), ks, _ptr(out, _DP),
+                T, start_pos, num_heads, num_kv_heads, head_dim, window,
+                nthreads or default_threads())
         if rc != 0:
             raise ValueError(f"oracle_prefill_attention returned {rc}")
         return out
 
     def rows(self, q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, row_t, row_h,
-             window=0, q_row_stride=None, kv_head_stride=None, nthreads=None):
+             window=0, q_row_stride=None, kv_head_stride=None, nthreads=None, ring_slots=0):
         """Rows (row_t[i], row_h[i]) only; returns fp64 [len(row_t), head_dim]."""
         q, k, v = _f32(q), _f32(k), _f32(v)
         qs, ks = self._strides(q, k, T, start_pos, num_heads, head_dim,
-                               q_row_stride, kv_head_stride)
-        _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks)
+                               q_row_stride, kv_head_stride, ring_slots)
+        _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks, ring_slots)
         rt = np.ascontiguousarray(row_t, dtype=np.int32)
         rh = np.ascontiguousarray(row_h, dtype=np.int32)
         if rt.shape != rh.shape or rt.ndim != 1:
             raise ValueError("row_t and row_h must be 1-D and of equal length")
         out = np.empty((rt.size, head_dim), dtype=np.float64)
-        rc = self.lib.oracle_prefill_attention_rows(
-            _ptr(q, _FP), qs, _ptr(k, _FP), _ptr(v, _FP), ks, _ptr(rt, _IP), _ptr(rh, _IP),
-            rt.size, _ptr(out, _DP), T, start_pos, num_heads, num_kv_heads, head_dim, window,
-            nthreads or default_threads())
+        rc = self.lib.oracle_prefill_attention_rows_ring(
+            _ptr(q, _FP), qs, _ptr(k, _FP), _ptr(v, _FP), ks, int(ring_slots), _ptr(rt, _IP),
+            _ptr(rh, _IP), rt.size, _ptr(out, _DP), T, start_pos, num_heads, num_kv_heads,
+            head_dim, window, nthreads or default_threads())
         if rc != 0:
             raise ValueError(f"oracle_prefill_attention_rows returned {rc}")
         return out
@@ -147,10 +162,10 @@ class Oracle:
         return first.value, probs[:n].copy()
 
 
-def _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks):
-    L = start_pos + T
+def _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks, ring_slots=0):
+    rows = ring_slots or (start_pos + T)
     need_q = (T - 1) * qs + num_heads * head_dim
-    need_kv = (num_kv_heads - 1) * ks + L * head_dim
+    need_kv = (num_kv_heads - 1) * ks + rows * head_dim
     if q.size < need_q:
         raise ValueError(f"q holds {q.size} elements, the chunk needs {need_q}")
     if k.size < need_kv or v.size < need_kv:

@@ -39,6 +39,14 @@
  *       positions has kv_head_stride = capacity*head_dim)
  *   out element (t, h, d) at out[(t*num_heads + h)*head_dim + d]
  *
+ * Ring caches (the *_ring entry points).  Requirement R4 of the TensorSharp
+ * page (section 4, "Requirements to enable replay") has sliding-window
+ * layers write position pos into slot pos % (ring size) of a circular cache.
+ * There key j of kv head kh is element (kh, j % ring_slots, d); nothing else
+ * changes.  The ring must hold every key the chunk reads at the same time,
+ * min(L, window + T - 1) slots (L for window 0); a shorter ring is an invalid
+ * argument.
+ *
  * Inputs are fp32 storage.  bf16 and fp16 values widen exactly to fp32, so
  * callers holding those types pass their fp32 images.  Every product and sum
  * is done in fp64 (the page's "independent f64 CPU recompute",
@@ -63,6 +71,7 @@ struct problem {
     int64_t q_row_stride;   /* elements between consecutive query tokens  */
     int64_t kv_head_stride; /* elements between consecutive kv heads      */
     int T, start_pos, num_heads, num_kv_heads, head_dim, window;
+    int ring;               /* ring slots per kv head; 0: key j in row j */
 };
 
 static int check_problem(const struct problem *P)
@@ -73,8 +82,23 @@ static int check_problem(const struct problem *P)
     if (P->num_heads % P->num_kv_heads != 0) return -1;
     if (P->window < 0) return -1;
     if (P->q_row_stride < (int64_t)P->num_heads * P->head_dim) return -1;
-    if (P->kv_head_stride < (int64_t)(P->start_pos + P->T) * P->head_dim) return -1;
+    if (P->ring < 0) return -1;
+    const int64_t L = (int64_t)P->start_pos + P->T;
+    if (P->ring > 0) {
+        const int64_t need = P->window > 0 && (int64_t)P->window + P->T - 1 < L
+                                 ? (int64_t)P->window + P->T - 1 : L;
+        if (P->ring < need) return -1;
+        if (P->kv_head_stride < (int64_t)P->ring * P->head_dim) return -1;
+    } else if (P->kv_head_stride < L * P->head_dim) {
+        return -1;
+    }
     return 0;
+}
+
+/* Row of key j in its kv head's block: j, or its slot in a ring cache. */
+static int64_t key_row(const struct problem *P, int j)
+{
+    return P->ring > 0 ? j % P->ring : j;
 }
 
 /* First valid key of the query at absolute position pos. */
@@ -103,7 +127,7 @@ static void attend_row(const struct problem *P, int t, int h, double *scores, do
 
     /* scores over the valid keys lo..=pos, scaled before the softmax */
     for (int j = lo; j <= pos; ++j) {
-        const float *k_row = k_head + (int64_t)j * D;
+        const float *k_row = k_head + key_row(P, j) * D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += (double)q_row[d] * (double)k_row[d];
@@ -127,7 +151,7 @@ static void attend_row(const struct problem *P, int t, int h, double *scores, do
         out_row[d] = 0.0;
     for (int j = lo; j <= pos; ++j) {
         const double p = scores[j - lo];
-        const float *v_row = v_head + (int64_t)j * D;
+        const float *v_row = v_head + key_row(P, j) * D;
         for (int d = 0; d < D; ++d)
             out_row[d] += p * (double)v_row[d];
     }
@@ -229,10 +253,30 @@ int oracle_prefill_attention(const float *q, int64_t q_row_stride,
                              int head_dim, int window, int nthreads)
 {
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0};
     if (check_problem(&P) || !out) return -1;
     return run_rows(&P, NULL, NULL, (int64_t)T * num_heads, out, nthreads);
 }
+
+/* Whole chunk over a ring cache of ring_slots slots per kv head. */
+int oracle_prefill_attention_ring(const float *q, int64_t q_row_stride,
+                                  const float *k_ring, const float *v_ring, int64_t kv_head_stride,
+                                  int ring_slots, double *out, int T, int start_pos,
+                                  int num_heads, int num_kv_heads, int head_dim, int window,
+                                  int nthreads)
+{
+    struct problem P = {q, k_ring, v_ring, q_row_stride, kv_head_stride,
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots};
+    if (ring_slots < 1 || check_problem(&P) || !out) return -1;
+    return run_rows(&P, NULL, NULL, (int64_t)T * num_heads, out, nthreads);
+}
+
+int oracle_prefill_attention_rows_ring(const float *q, int64_t q_row_stride,
+                                       const float *k_cache, const float *v_cache,
+                                       int64_t kv_head_stride, int ring_slots,
+                                       const int32_t *row_t, const int32_t *row_h, int64_t nrows,
+                                       double *out, int T, int start_pos, int num_heads,
+                                       int num_kv_heads, int head_dim, int window, int nthreads);
 
 /*
  * Selected rows (row_t[i], row_h[i]) of the same chunk: out is [nrows][head_dim].
@@ -243,8 +287,21 @@ int oracle_prefill_attention_rows(const float *q, int64_t q_row_stride,
                                   double *out, int T, int start_pos, int num_heads, int num_kv_heads,
                                   int head_dim, int window, int nthreads)
 {
+    return oracle_prefill_attention_rows_ring(q, q_row_stride, k_cache, v_cache, kv_head_stride, 0,
+                                              row_t, row_h, nrows, out, T, start_pos, num_heads,
+                                              num_kv_heads, head_dim, window, nthreads);
+}
+
+/* Selected rows over a ring cache (ring_slots 0: the linear layout). */
+int oracle_prefill_attention_rows_ring(const float *q, int64_t q_row_stride,
+                                       const float *k_cache, const float *v_cache,
+                                       int64_t kv_head_stride, int ring_slots,
+                                       const int32_t *row_t, const int32_t *row_h, int64_t nrows,
+                                       double *out, int T, int start_pos, int num_heads,
+                                       int num_kv_heads, int head_dim, int window, int nthreads)
+{
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots};
     if (check_problem(&P) || !out || !row_t || !row_h || nrows < 1) return -1;
     for (int64_t i = 0; i < nrows; ++i)
         if (row_t[i] < 0 || row_t[i] >= T || row_h[i] < 0 || row_h[i] >= num_heads) return -1;
@@ -263,7 +320,7 @@ int oracle_row_probabilities(const float *q, int64_t q_row_stride,
                              int head_dim, int window)
 {
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0};
     if (check_problem(&P) || !probs || !first) return -1;
     if (t < 0 || t >= T || h < 0 || h >= num_heads) return -1;
     double *out_row = (double *)malloc(sizeof(double) * (size_t)head_dim);

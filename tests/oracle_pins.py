@@ -20,6 +20,10 @@ when that build disagrees with what the pages or the mathematics fix:
                 keys on its edges do; a per-kv-head shift of every key leaves
                 the output unchanged even when the raw scores would overflow
                 exp
+  ring cache    keys written in order into slot pos % R (the TensorSharp
+                page, section 4, requirement R4): the closed form above still
+                holds, and a chunk loop through the ring gives the rows of the
+                one-shot prefill over the linear cache, bit for bit
 
 The module is shared by ``test_oracle_pins.py`` (the real oracle must pass
 every pin) and ``test_oracle_mutants.py`` (each planted mistake must fail at
@@ -318,6 +322,73 @@ def pin_strided_layouts(orc):
     assert np.array_equal(sub, packed[rows_t, rows_h])
 
 
+def _ring_writes(rows, ring_slots, upto, ring=None):
+    """Write keys 0 .. upto-1 of rows [KVH, positions, D] one by one into slot
+    pos % ring_slots of a ring (NaN where nothing was written), as the cache
+    writes of a sliding-window layer do."""
+    if ring is None:
+        ring = np.full((rows.shape[0], ring_slots, rows.shape[2]), np.nan, np.float32)
+    for j in range(upto):
+        ring[:, j % ring_slots] = rows[:, j]
+    return ring
+
+
+def pin_ring_closed_form(orc):
+    """Ring cache (key j in slot j % R, written in order): with q = 0 and
+    V[kh, j] = j + 1000*kh the output is still (lo + pos)/2 + 1000*kv_head(h)."""
+    for H, KVH, D, T, sp, W, R in ((4, 2, 4, 6, 20, 5, 10), (4, 1, 8, 9, 31, 3, 11),
+                                   (2, 2, 2, 5, 0, 4, 8), (4, 2, 4, 1, 57, 7, 7)):
+        L = sp + T
+        G = H // KVH
+        q = np.zeros((T, H * D), np.float32)
+        rng = np.random.default_rng(RNG_SEED + 12)
+        k = _rand(rng, (KVH, L, D))
+        v = np.empty((KVH, L, D), np.float32)
+        for kh in range(KVH):
+            v[kh] = (np.arange(L)[:, None] + 1000.0 * kh).astype(np.float32)
+        out = orc.attention(q, _ring_writes(k, R, L), _ring_writes(v, R, L), T, sp, H, KVH, D,
+                            window=W, ring_slots=R)
+        for t in range(T):
+            pos = sp + t
+            lo = max(0, pos - W + 1)
+            for h in range(H):
+                want = (lo + pos) / 2.0 + 1000.0 * (h // G)
+                assert np.abs(out[t, h] - want).max() <= 1e-9, (t, h, R, out[t, h, 0], want)
+
+
+def pin_ring_chunked_equals_linear(orc):
+    """A prompt prefilled chunk by chunk through a ring of window + T - 1 slots
+    (each chunk's keys written before its call, older ones overwritten, unwritten
+    slots NaN) gives the rows of the one-shot prefill over the linear cache."""
+    rng = np.random.default_rng(RNG_SEED + 13)
+    H, KVH, D, N, W = 4, 2, 8, 40, 6
+    q, k, v = _case(rng, H, KVH, D, N, 0)
+    full = orc.attention(q, k, v, N, 0, H, KVH, D, window=W)
+    for chunks, extra in (((7, 7, 1, 12, 13), 0), ((9, 9, 9, 9, 4), 3)):
+        R = W + max(chunks) - 1 + extra
+        kr = vr = None
+        start = 0
+        for T in chunks:
+            kr = _ring_writes(k, R, start + T, kr)
+            vr = _ring_writes(v, R, start + T, vr)
+            got = orc.attention(q[start:start + T], kr, vr, T, start, H, KVH, D, window=W,
+                                ring_slots=R)
+            assert np.array_equal(got, full[start:start + T]), (chunks, start)
+            rows_t = np.array([0, T - 1])
+            rows_h = np.array([H - 1, 0])
+            sub = orc.rows(q[start:start + T], kr, vr, T, start, H, KVH, D, rows_t, rows_h,
+                           window=W, ring_slots=R)
+            assert np.array_equal(sub, full[start + rows_t, rows_h])
+            start += T
+    # a ring one slot short of what a chunk reads at once is refused
+    try:
+        orc.attention(q[:8], k[:, :8], v[:, :8], 8, 0, H, KVH, D, window=W, ring_slots=W + 8 - 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("short ring accepted")
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -332,4 +403,6 @@ ALL_PINS = [
     pin_shift_invariance,
     pin_hand_example,
     pin_strided_layouts,
+    pin_ring_closed_form,
+    pin_ring_chunked_equals_linear,
 ]

@@ -38,7 +38,11 @@ MUTANTS = [
                                "P->v + (int64_t)kv_h * (P->start_pos + P->T) * D", 1)]),
     ("softmax_denominator_off", [("scores[i] = scores[i] / total;",
                                   "scores[i] = scores[i] / (total + 1e-3);", 1)]),
-    ("value_row_relative_to_lo", [("v_head + (int64_t)j * D", "v_head + (int64_t)(j - lo) * D", 1)]),
+    ("value_row_relative_to_lo", [("v_head + key_row(P, j) * D", "v_head + key_row(P, j - lo) * D", 1)]),
+    ("ring_slot_off_by_one", [("return P->ring > 0 ? j % P->ring : j;",
+                               "return P->ring > 0 ? (j + 1) % P->ring : j;", 1)]),
+    ("ring_keys_of_value_slots", [("const float *k_row = k_head + key_row(P, j) * D;",
+                                   "const float *k_row = k_head + (P->ring > 0 ? (j + P->ring - 1) % P->ring : j) * D;", 1)]),
     ("query_row_of_first_token", [("const int pos = P->start_pos + t;", "const int pos = P->start_pos;", 1)]),
 ]
 
