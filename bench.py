@@ -168,8 +168,18 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
         return t.view(torch.bfloat16 if wl.dtype == "bf16" else torch.float16)
 
-    k = dev_tensor(x.k_store)
-    v = dev_tensor(x.v_store)
+    if wl.ring:
+        # the cache as a ring of wl.ring slots per kv head (key j in slot j % ring),
+        # as left by writing the keys up to the chunk's last one
+        assert len(wl.chunks) == 1
+        L = wl.chunks[0][1] + wl.chunks[0][0]
+        k = dev_tensor(workloads.ring_cache(x.k_store, wl.ring, L, 0))
+        v = dev_tensor(workloads.ring_cache(x.v_store, wl.ring, L, 0))
+        kv_stride, ring_slots = wl.ring * D, wl.ring
+    else:
+        k = dev_tensor(x.k_store)
+        v = dev_tensor(x.v_store)
+        kv_stride, ring_slots = wl.capacity * D, None
     # each chunk's C-ABI call with its arguments checked and marshalled once, so
     # that the timed loop issues only the calls (µs-scale kernels would
     # otherwise wait on the host)
@@ -179,8 +189,8 @@ def main():
         out = torch.empty(T, H * D, dtype=torch.float32, device=dev)
         nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
         ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-        calls.append(pa.PreparedCall(q, H * D, k, v, wl.capacity * D, out, H * D, T, sp, H, KVH, D, W,
-                                     workspace=ws))
+        calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
+                                     workspace=ws, ring_slots=ring_slots))
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 

@@ -53,6 +53,8 @@ def load():
         fn.restype = I
     lib.prefill_attn_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, P, SZ, P]
     lib.prefill_attn_ex.restype = I
+    lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, P, SZ, P]
+    lib.prefill_attn_ring_ex.restype = I
     lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.prefill_attn_workspace_bytes.restype = SZ
     lib.prefill_attn_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I64), I]
@@ -143,7 +145,8 @@ def prefill_attn(q, k_cache, v_cache, out, T, start_pos, num_heads, num_kv_heads
 
 
 class PreparedCall:
-    """prefill_attn_ex with its arguments checked and marshalled once.
+    """prefill_attn_ex (prefill_attn_ring_ex when ring_slots is given) with
+    its arguments checked and marshalled once.
 
     For callers that launch the same call repeatedly (a chunk loop, a
     benchmark): calling the object issues just the C-ABI call.  The tensors
@@ -152,30 +155,34 @@ class PreparedCall:
 
     def __init__(self, q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                  start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
-                 stream=None):
+                 stream=None, ring_slots=None):
         dt = _dtype_of(q)
         if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
             raise TypeError("q, k_cache and v_cache must share one storage type")
-        L = start_pos + T
+        rows = start_pos + T if ring_slots is None else ring_slots
         _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
-        _need(k_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "k_cache")
-        _need(v_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "v_cache")
+        _need(k_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "k_cache")
+        _need(v_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "v_cache")
         _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
         ws_ptr, ws_bytes = None, 0
         if workspace is not None:
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        self._fn = load().prefill_attn_ex
-        self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
-                      v_cache.data_ptr(), kv_head_stride, out.data_ptr(), out_row_stride, T,
-                      start_pos, num_heads, num_kv_heads, head_dim, window, ws_ptr, ws_bytes,
-                      _stream(stream))
+        head = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                v_cache.data_ptr(), kv_head_stride)
+        tail = (out.data_ptr(), out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim,
+                window, ws_ptr, ws_bytes, _stream(stream))
+        if ring_slots is None:
+            self._name, self._fn, self._args = "prefill_attn_ex", load().prefill_attn_ex, head + tail
+        else:
+            self._name, self._fn = "prefill_attn_ring_ex", load().prefill_attn_ring_ex
+            self._args = head + (int(ring_slots),) + tail
         self._keep = (q, k_cache, v_cache, out, workspace)
         self.out = out
 
     def __call__(self):
         st = self._fn(*self._args)
         if st != PA_OK:
-            raise PrefillAttnError(st, "prefill_attn_ex")
+            raise PrefillAttnError(st, self._name)
         return self.out
 
 
@@ -185,3 +192,12 @@ def prefill_attn_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_
     """Strided call; workspace is a device tensor (any dtype) or None."""
     return PreparedCall(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                         start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream)()
+
+
+def prefill_attn_ring_ex(q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_slots, out,
+                         out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window=0,
+                         workspace=None, stream=None):
+    """Strided call over a ring cache: key j in slot j % ring_slots of each kv head."""
+    return PreparedCall(q, q_row_stride, k_ring, v_ring, kv_head_stride, out, out_row_stride, T,
+                        start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream,
+                        ring_slots=ring_slots)()

@@ -88,7 +88,9 @@ struct Params {
     int n_items;      // nq * KVH * S work-groups
     float c;          // log2(e) / sqrt(head_dim)
     int order;        // 1: within a die, longest query tiles first then shortest first; 0: longest first
-    int kv_bytes;     // bytes of the L valid rows of one kv head (16-bit kernels)
+    int kv_bytes;     // bytes of the L valid rows (linear) or of the ring slots of one kv head
+    int L;            // keys of the call: start_pos + T
+    int ring;         // ring cache: key j sits in slot j % ring of its kv head; 0: row j
     const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
     int vop_kt_lo;         // first KV tile held in vop
     int vop_tiles;         // KV tiles per kv head held in vop
@@ -289,6 +291,51 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bytes) 
 
 [[maybe_unused]] __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Largest K/V block per kv head the 16-bit kernels address (32-bit buffer
+// offsets with room for a tile past its end), and an offset past any such
+// range: loads there return zeros.
+constexpr int kMaxHeadBytes = 0x7FE00000;
+constexpr int kPastRange = 0x7FF00000;
+
+// Ring cache (sliding-window layers): key j of a kv head sits in slot
+// j % ring.  lin[i] is the offset lane load i of a tile would have in a
+// linear cache, row * row_bytes + chunk; the function sets off[i] and returns
+// the scalar offset that go with it for the tile whose first key is j0.
+// When the ring is a multiple of the tile and the tile ends before L, the
+// tile's rows sit in consecutive slots from s0 = j0 % ring: the linear
+// offsets plus s0 rows.  Otherwise each row finds its slot s0 + row, wrapped
+// once past the ring's end (rings of at least BK slots; the wrap test
+// compares lin itself, since chunk < row_bytes) or reduced by division, and
+// rows at keys >= L read as zero, like the rows past L of a linear cache.
+template <int N>
+__device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_bytes,
+                                   const int (&lin)[N], int (&off)[N]) {
+    const int s0 = j0 % p.ring;
+    if (p.ring % BK == 0 && j0 + BK <= p.L) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) off[i] = lin[i];
+        return s0 * row_bytes;
+    }
+    if (p.ring >= BK) {
+        const int wrap_at = (p.ring - s0) * row_bytes, base = s0 * row_bytes;
+        const int back = p.ring * row_bytes;
+#pragma unroll
+        for (int i = 0; i < N; ++i) off[i] = lin[i] + base - (lin[i] >= wrap_at ? back : 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int row = lin[i] / row_bytes;
+            off[i] = ((s0 + row) % p.ring) * row_bytes + (lin[i] - row * row_bytes);
+        }
+    }
+    if (j0 + BK > p.L) {
+        const int end = (p.L - j0) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < N; ++i) off[i] = lin[i] >= end ? kPastRange : off[i];
+    }
+    return 0;
+}
+
 // LDS operand reads issued as inline assembly.  The wait-count pass treats
 // the builtin transposed read as one that may alias any LDS DMA still in
 // flight and puts a vmcnt(0) in front of it, which would stall every P.V
@@ -397,7 +444,8 @@ struct Ones {
 //        d = 16*block + l%16
 template <int D, int BK, bool M16>
 __global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_t kv_head_stride,
-                                                       int L, int kt_lo, int ntiles, uint16_t *vop) {
+                                                       int L, int ring, int kt_lo, int ntiles,
+                                                       uint16_t *vop) {
     constexpr int PITCH = D + 2;               // LDS row pitch (elements): column reads spread banks
     constexpr int CHUNKS = BK * D / 8;
     __shared__ uint32_t t32[BK * PITCH / 2];
@@ -408,7 +456,8 @@ __global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_
     for (int cidx = threadIdx.x; cidx < CHUNKS; cidx += 256) {
         const int key = cidx / (D / 8), c8 = cidx % (D / 8);
         const int j = j0 + key;
-        const u32x4 val = j < L ? *(const u32x4 *)(src + (int64_t)j * D + 8 * c8) : u32x4{0, 0, 0, 0};
+        const int64_t slot = ring ? j % ring : j;      // ring cache: key j in slot j % ring
+        const u32x4 val = j < L ? *(const u32x4 *)(src + slot * D + 8 * c8) : u32x4{0, 0, 0, 0};
         uint32_t *row = t32 + (key * PITCH + 8 * c8) / 2;
         row[0] = val[0];
         row[1] = val[1];
@@ -441,7 +490,7 @@ __global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_
     }
 }
 
-template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD>
+template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD, bool RING>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -523,13 +572,26 @@ void attn_fwd16(Params p) {
     const float c = p.c;
 
     auto issue = [&](int kt, int kdst, int vdst) {
-        const int base = kt * BK * D * 2;
+        if constexpr (!RING) {
+            const int base = kt * BK * D * 2;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+            }
+        } else {
+            int ko[LOADS], vo[LOADS];
+            const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
+            const int vs = ring_offsets(p, kt * BK, BK, D * 2, voff, vo);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, ko[i], ks, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, vo[i], vs, 0, 0);
+            }
         }
     };
 
@@ -701,7 +763,7 @@ __device__ inline int swz_v16(int row) {
     return 2 * (row & 7);
 }
 
-template <class Ty, int D, int BK, bool VPACK, int KSPLIT>
+template <class Ty, int D, int BK, bool VPACK, int KSPLIT, bool RING>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -792,14 +854,31 @@ void attn_fwd16_r16(Params p) {
     const float c = p.c;
 
     auto issue = [&](int kt, int kdst, int vdst) {
-        const int base = kt * BK * D * 2;
-        const int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : base;
+        if constexpr (!RING) {
+            const int base = kt * BK * D * 2;
+            const int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : base;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
+            }
+        } else {
+            // the operand-ordered V copy is linear in the call's tiles; K (and
+            // V read in place) come from the ring slots
+            int ko[LOADS], vo[LOADS];
+            const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
+            int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : 0;
+            if constexpr (!VPACK) vbase_t = ring_offsets(p, kt * BK, BK, D * 2, voff, vo);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, ko[i], ks, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, VPACK ? voff[i] : vo[i],
+                    vbase_t, 0, 0);
+            }
         }
     };
 
@@ -1067,7 +1146,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
             const int idx = tid + i * kThreads;
             const int key = idx / (D / 4), c4 = idx % (D / 4);
             const int j = j0 + key;
-            kbuf[i] = j < L ? *(const f32x4 *)(kbase + (int64_t)j * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int64_t jr = p.ring ? j % p.ring : j;   // ring cache: key j in slot j % ring
+            kbuf[i] = j < L ? *(const f32x4 *)(kbase + jr * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -1077,7 +1157,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + 4 * kq + u;
-                vbuf[i][u] = j < L ? *(const f32x4 *)(vbase + (int64_t)j * D + 4 * c4)
+                const int64_t jr = p.ring ? j % p.ring : j;
+                vbuf[i][u] = j < L ? *(const f32x4 *)(vbase + jr * D + 4 * c4)
                                    : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -1203,7 +1284,7 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
 // ---- host side -----------------------------------------------------------------------
 
 using KernelFn = void (*)(Params);
-using PackFn = void (*)(const uint16_t *, int64_t, int, int, int, uint16_t *);
+using PackFn = void (*)(const uint16_t *, int64_t, int, int, int, int, uint16_t *);
 
 struct Variant {
     int dtype, D, BK;
@@ -1211,27 +1292,28 @@ struct Variant {
     int threads;               // work-group size (4 or 8 wavefronts)
     int rows;                  // (token, head) rows per work-group
     int ksplit;                // 2: the tile's keys are split between two wavefront halves
-    KernelFn fn;
+    KernelFn fn;               // linear caches
+    KernelFn fn_ring;          // ring caches (key j in slot j % ring)
     PackFn pack;               // V operand-order pass (16-bit inputs), else null
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1>, nullptr},
-    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2>, nullptr},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2>, nullptr},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1>, nullptr},
-    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2>, nullptr},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<32, 32>, nullptr},
-    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<64, 32>, nullptr},
-    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<128, 32>, nullptr},
-    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, nullptr},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2, false>, attn_fwd16<Bf16, 32, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2, false>, attn_fwd16<Bf16, 64, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2, false>, attn_fwd16<Bf16, 128, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1, false>, attn_fwd16_r16<Bf16, 256, 64, false, 1, true>, nullptr},
+    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2, false>, attn_fwd16_r16<Bf16, 256, 32, false, 2, true>, nullptr},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1, false>, attn_fwd16_r16<Bf16, 512, 32, true, 1, true>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2, false>, attn_fwd16<F16, 32, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2, false>, attn_fwd16<F16, 64, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2, false>, attn_fwd16<F16, 128, 64, 4, 2, true>, nullptr},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1, false>, attn_fwd16_r16<F16, 256, 64, false, 1, true>, nullptr},
+    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2, false>, attn_fwd16_r16<F16, 256, 32, false, 2, true>, nullptr},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1, false>, attn_fwd16_r16<F16, 512, 32, true, 1, true>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<32, 32>, attn_fwd32<32, 32>, nullptr},
+    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<64, 32>, attn_fwd32<64, 32>, nullptr},
+    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<128, 32>, attn_fwd32<128, 32>, nullptr},
+    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, attn_fwd32<256, 32>, nullptr},
 };
 
 using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
@@ -1285,8 +1367,6 @@ int check_shape(int dtype, int T, int start_pos, int H, int KVH, int D, int wind
     if ((int64_t)start_pos + T > INT32_MAX) return PA_ERR_INVALID_ARG;
     if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16) return PA_ERR_UNSUPPORTED;
     if (H / KVH > kRowsPerGroup) return PA_ERR_UNSUPPORTED;
-    // the 16-bit kernels address one kv head's rows with 32-bit buffer offsets
-    if (dtype != PA_DTYPE_F32 && ((int64_t)start_pos + T) * D * 2 > INT32_MAX) return PA_ERR_UNSUPPORTED;
     if (!find_variant(dtype, D)) return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -1377,9 +1457,11 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+// ring: slots per kv head of a ring cache (key j in slot j % ring), 0 for a
+// linear cache (key j in row j).
 int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const void *k,
-           const void *v, int64_t kv_head_stride, float *out, int64_t out_row_stride, int T,
-           int start_pos, int H, int KVH, int D, int window, void *ws, hipStream_t stream) {
+           const void *v, int64_t kv_head_stride, int ring, float *out, int64_t out_row_stride,
+           int T, int start_pos, int H, int KVH, int D, int window, void *ws, hipStream_t stream) {
     Params p;
     p.q = q;
     p.k = k;
@@ -1405,14 +1487,18 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
     p.order = pl.var->groups_per_cu == 2 ? 1 : 0;
-    p.kv_bytes = (int)std::min<int64_t>(((int64_t)start_pos + T) * D * elem_bytes(dtype), INT32_MAX);
+    p.L = start_pos + T;
+    p.ring = ring;
+    p.kv_bytes = (int)std::min<int64_t>((ring ? (int64_t)ring : (int64_t)start_pos + T) * D *
+                                            elem_bytes(dtype), INT32_MAX);
     if (pl.var->pack) {
         hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream,
-                           (const uint16_t *)v, kv_head_stride, start_pos + T, pl.vop_kt_lo,
+                           (const uint16_t *)v, kv_head_stride, start_pos + T, ring, pl.vop_kt_lo,
                            pl.vop_tiles, (uint16_t *)ws);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     }
-    hipLaunchKernelGGL(pl.var->fn, dim3(pl.items), dim3(pl.var->threads), 0, stream, p);
+    hipLaunchKernelGGL(ring ? pl.var->fn_ring : pl.var->fn, dim3(pl.items), dim3(pl.var->threads), 0,
+                       stream, p);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (pl.S > 1) {
         const int64_t n = (int64_t)T * H * (D / 4);
@@ -1424,17 +1510,21 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     return PA_OK;
 }
 
+// rows_per_head: the rows the kernels address in each kv head's block (L for
+// a linear cache, the slot count of a ring).
 int check_args(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
-               int64_t kv_head_stride, const float *out, int64_t out_row_stride, int T,
-               int start_pos, int H, int KVH, int D, int window) {
+               int64_t kv_head_stride, int64_t rows_per_head, const float *out,
+               int64_t out_row_stride, int T, int start_pos, int H, int KVH, int D, int window) {
     if (!q || !k || !v || !out) return PA_ERR_INVALID_ARG;
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st == PA_ERR_INVALID_ARG) return st;
     const int64_t row = (int64_t)H * D;
     if (q_row_stride < row || out_row_stride < row) return PA_ERR_INVALID_ARG;
-    if (kv_head_stride < ((int64_t)start_pos + T) * D) return PA_ERR_INVALID_ARG;
+    if (kv_head_stride < rows_per_head * D) return PA_ERR_INVALID_ARG;
     if (st != PA_OK) return st;
     const int eb = elem_bytes(dtype);
+    // the 16-bit kernels address one kv head's rows with 32-bit buffer offsets
+    if (dtype != PA_DTYPE_F32 && rows_per_head * D * eb > kMaxHeadBytes) return PA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_UNSUPPORTED;
     if ((q_row_stride * eb) % 16 || (kv_head_stride * eb) % 16 || (out_row_stride * 4) % 16)
         return PA_ERR_UNSUPPORTED;
@@ -1479,7 +1569,8 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
                int start_pos, int H, int KVH, int D, int window, void *stream) {
     const int64_t row = (int64_t)H * D;
     const int64_t kvs = ((int64_t)start_pos + T) * D;
-    int st = check_args(dtype, q, row, k, v, kvs, out, row, T, start_pos, H, KVH, D, window);
+    int st = check_args(dtype, q, row, k, v, kvs, (int64_t)start_pos + T, out, row, T, start_pos, H,
+                        KVH, D, window);
     if (st != PA_OK) return st;
     Plan pl;
     st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
@@ -1487,8 +1578,24 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
     void *ws = nullptr;
     st = scratch_for(pl.ws_bytes, &ws);
     if (st != PA_OK) return st;
-    return launch(pl, dtype, q, row, k, v, kvs, out, row, T, start_pos, H, KVH, D, window, ws,
+    return launch(pl, dtype, q, row, k, v, kvs, 0, out, row, T, start_pos, H, KVH, D, window, ws,
                   (hipStream_t)stream);
+}
+
+// Plan, workspace check and launch of the strided entry points (arguments checked).
+int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
+           int64_t kv_head_stride, int ring, float *out, int64_t out_row_stride, int T,
+           int start_pos, int H, int KVH, int D, int window, void *workspace,
+           size_t workspace_bytes, void *stream) {
+    Plan pl;
+    const int st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
+    if (st != PA_OK) return st;
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
+    }
+    return launch(pl, dtype, q, q_row_stride, k, v, kv_head_stride, ring, out, out_row_stride, T,
+                  start_pos, H, KVH, D, window, workspace, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -1523,19 +1630,33 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *
                     int64_t out_row_stride, int T, int start_pos, int num_heads,
                     int num_kv_heads, int head_dim, int window, void *workspace,
                     size_t workspace_bytes, void *stream) {
-    int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, out,
+    int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride,
+                        (int64_t)start_pos + T, out, out_row_stride, T, start_pos, num_heads,
+                        num_kv_heads, head_dim, window);
+    if (st != PA_OK) return st;
+    return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, 0, out, out_row_stride,
+                  T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+                  workspace_bytes, stream);
+}
+
+int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_ring,
+                         const void *v_ring, int64_t kv_head_stride, int ring_slots, float *out,
+                         int64_t out_row_stride, int T, int start_pos, int num_heads,
+                         int num_kv_heads, int head_dim, int window, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (ring_slots < 1) return PA_ERR_INVALID_ARG;
+    int st = check_args(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_slots, out,
                         out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window);
     if (st != PA_OK) return st;
-    Plan pl;
-    st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl);
-    if (st != PA_OK) return st;
-    if (pl.ws_bytes > 0) {
-        if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
-        if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
-    }
-    return launch(pl, dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, out,
-                  out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window,
-                  workspace, (hipStream_t)stream);
+    // the ring must hold every key the chunk reads at once: the window before
+    // the chunk's first query through its last key
+    const int64_t L = (int64_t)start_pos + T;
+    const int64_t need = window > 0 ? std::min<int64_t>(L, (int64_t)window + T - 1) : L;
+    if (ring_slots < need) return PA_ERR_INVALID_ARG;
+    // a ring at least as long as the call is a linear cache (slot j holds key j)
+    return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride,
+                  ring_slots >= L ? 0 : ring_slots, out, out_row_stride, T, start_pos, num_heads,
+                  num_kv_heads, head_dim, window, workspace, workspace_bytes, stream);
 }
 
 size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_heads,

@@ -114,8 +114,31 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride,
                     int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Scratch bytes prefill_attn_ex needs for these arguments (0: none).
- * Returns 0 as well for arguments that are invalid or unsupported.
+ * Ring cache form (sliding-window layers).  The TensorSharp page "Design:
+ * closing the Gemma-4 long-prompt prefill gap", section 4, requirement R4,
+ * has sliding-window layers write the K/V of position pos into slot
+ * pos % (ring size) of a circular cache instead of row pos.  Here key j of
+ * kv head kh is read from
+ *     k_ring[kh*kv_head_stride + (j % ring_slots)*head_dim + d]   (v_ring alike)
+ * and everything else is prefill_attn_ex.  The caller has written the
+ * chunk's own keys before the call, so every key the chunk reads must be
+ * resident at once: ring_slots >= min(L, window + T - 1) for window > 0 and
+ * ring_slots >= L for window 0 (a ring that short cannot hold them and the
+ * call returns PA_ERR_INVALID_ARG; for T = 1, window slots suffice).  Slots
+ * that hold no key of [0, L) are never read, so they may hold anything,
+ * NaN included.  kv_head_stride >= ring_slots*head_dim.  The workspace is
+ * the one prefill_attn_workspace_bytes gives for the same shape.
+ */
+int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride,
+                         const void *k_ring, const void *v_ring, int64_t kv_head_stride,
+                         int ring_slots, float *out, int64_t out_row_stride,
+                         int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                         int window, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Scratch bytes prefill_attn_ex (or prefill_attn_ring_ex) needs for these
+ * arguments (0: none).  Returns 0 as well for arguments that are invalid or
+ * unsupported.
  */
 size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_heads,
                                     int num_kv_heads, int head_dim, int window);

@@ -18,8 +18,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = pa.header_functions()
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
-                          "prefill_attn_ex", "prefill_attn_workspace_bytes", "prefill_attn_plan",
-                          "prefill_attn_strerror"}
+                          "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
+                          "prefill_attn_plan", "prefill_attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -118,3 +118,28 @@ def test_prepared_call_rejects_host_tensors():
         pa.PreparedCall(q, 64, kv, kv, 4 * 32, out, 64, 4, 0, 2, 1, 32)
     with pytest.raises(ValueError):
         pa.prefill_attn_ex(q, 64, kv, kv, 4 * 32, out, 64, 4, 0, 2, 1, 32)
+
+
+def test_ring_arguments(lib):
+    """The ring form refuses rings that cannot hold every key the chunk reads,
+    a head stride below ring_slots*head_dim and a non-positive slot count,
+    before anything is enqueued (fake device pointers are never touched)."""
+    rx = lib.prefill_attn_ring_ex
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    H, KVH, D, T, sp, W = 8, 4, 256, 64, 5000, 100
+
+    def call(ring, kvs=None, w=W, t=T, s=sp, dtype=1):
+        kvs = ring * D if kvs is None else kvs
+        return rx(dtype, FAKE, H * D, FAKE, FAKE, kvs, ring, FAKE, H * D, t, s, H, KVH, D, w,
+                  None, 0, None)
+
+    assert call(0) == E
+    assert call(-5) == E
+    assert call(W + T - 2) == E                    # one slot short of window + T - 1
+    assert call(W + T - 1, kvs=(W + T - 1) * D - 8) == E
+    assert call(3000, w=0) == E                    # no window: the ring must hold all L keys
+    assert call(W + T - 1, dtype=7) == U
+    # a ring too large for 32-bit buffer offsets of the 16-bit kernels
+    assert call(2 ** 22, w=0, s=2 ** 22 - T) == U
+    # every shape check of prefill_attn_ex applies too
+    assert call(W + T - 1, t=0) == E

@@ -199,15 +199,25 @@ def _run_workload(orc, name, n_random=64):
     wl = workloads.WORKLOADS[name]
     x = workloads.make_inputs(wl)
     H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
-    k = to_device(x.k_store, wl.dtype)
-    v = to_device(x.v_store, wl.dtype)
+    if not wl.ring:
+        k = to_device(x.k_store, wl.dtype)
+        v = to_device(x.v_store, wl.dtype)
     for ci, (T, sp) in enumerate(wl.chunks):
         q_store, q_f32 = x.q_rows(ci)
         q = to_device(q_store, wl.dtype)
         out = torch.empty(T, H * D, device=device())
         ws_b = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
         ws = torch.empty(ws_b, dtype=torch.uint8, device=device()) if ws_b else None
-        pa.prefill_attn_ex(q, H * D, k, v, wl.capacity * D, out, H * D, T, sp, H, KVH, D, W, workspace=ws)
+        if wl.ring:
+            # the ring as the cache writes up to this chunk's last key leave it
+            nan = np.uint16(0x7FC0) if wl.dtype == "bf16" else np.uint16(0x7E00)
+            k = to_device(workloads.ring_cache(x.k_store, wl.ring, sp + T, nan), wl.dtype)
+            v = to_device(workloads.ring_cache(x.v_store, wl.ring, sp + T, nan), wl.dtype)
+            pa.prefill_attn_ring_ex(q, H * D, k, v, wl.ring * D, wl.ring, out, H * D, T, sp, H, KVH,
+                                    D, W, workspace=ws)
+        else:
+            pa.prefill_attn_ex(q, H * D, k, v, wl.capacity * D, out, H * D, T, sp, H, KVH, D, W,
+                               workspace=ws)
         torch.cuda.synchronize()
         got = out.cpu().numpy().reshape(T, H, D)
         if T * H <= 64 * 1024 and (sp + T) * T * H * D <= 2e10:
@@ -241,3 +251,7 @@ def test_workload_gemma_global_bf16(orc):
 
 def test_workload_gemma_swa_bf16(orc):
     _run_workload(orc, "gemma_swa_bf16")
+
+
+def test_workload_gemma_swa_bf16_ring(orc):
+    _run_workload(orc, "gemma_swa_bf16_ring")

@@ -40,6 +40,7 @@ class Workload:
     std: float                       # inputs ~ N(0, 1) * std
     seed: int
     summary: str = ""
+    ring: int = 0                    # > 0: the GPU reads K/V from a ring of this many slots
 
     @property
     def q_tokens(self) -> int:
@@ -73,7 +74,26 @@ WORKLOADS = {
         "gemma_swa_bf16", "bf16", 8, 4, 256, 1024, ((2048, 129024),), 131072, 0.3, 105,
         "Gemma-style sliding-window layer, 8/4 heads, head_dim 256, window 1024, "
         "T=2048 at start_pos 129024"),
+    # the same layer and values, its K/V held in a ring cache of 3072 slots
+    # (window + T - 1 = 3071 keys are read at once)
+    "gemma_swa_bf16_ring": Workload(
+        "gemma_swa_bf16_ring", "bf16", 8, 4, 256, 1024, ((2048, 129024),), 131072, 0.3, 105,
+        "Gemma-style sliding-window layer as gemma_swa_bf16, K/V in a ring cache of 3072 slots "
+        "(key j in slot j % 3072)", ring=3072),
 }
+
+
+def ring_cache(rows: np.ndarray, ring_slots: int, L: int, fill) -> np.ndarray:
+    """The ring cache left by writing keys 0 .. L-1 of ``rows`` ([kv heads,
+    positions, head_dim]) one after another into slot pos % ring_slots: slot s
+    holds the newest key j < L with j % ring_slots == s; slots no key reached
+    hold ``fill``."""
+    kvh, _, d = rows.shape
+    ring = np.full((kvh, ring_slots, d), fill, dtype=rows.dtype)
+    first = max(0, L - ring_slots)
+    j = np.arange(first, L)
+    ring[:, j % ring_slots] = rows[:, first:L]
+    return ring
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
