@@ -91,6 +91,8 @@ class Oracle:
             _FP, _I64, _FP, _FP, _I64, _INT, _IP, _IP, _I64, _DP,
             _INT, _INT, _INT, _INT, _INT, _INT, _INT]
         lib.oracle_prefill_attention_rows_ring.restype = _INT
+        lib.oracle_kv_write.argtypes = [_FP, _FP, _I64, _FP, _FP, _I64, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_kv_write.restype = _INT
         self.lib = lib
 
     @staticmethod
@@ -160,6 +162,29 @@ class Oracle:
         if n < 0:
             raise ValueError(f"oracle_row_probabilities returned {n}")
         return first.value, probs[:n].copy()
+
+
+    def kv_write(self, k_src, v_src, src_row_stride, k_cache, v_cache, kv_head_stride, T,
+                 start_pos, num_kv_heads, head_dim, ring_slots=0):
+        """Store tokens 0..T-1 of k_src/v_src (fp32 images) in the caches, in
+        order: row start_pos + i, or slot (start_pos + i) % ring_slots.  The
+        caches (contiguous fp32 arrays) are updated in place."""
+        k_src, v_src = _f32(k_src), _f32(v_src)
+        for c in (k_cache, v_cache):
+            if c.dtype != np.float32 or not c.flags["C_CONTIGUOUS"]:
+                raise TypeError("caches must be contiguous float32 arrays")
+        rows = ring_slots or (start_pos + T)
+        need_src = (T - 1) * src_row_stride + num_kv_heads * head_dim
+        need_c = (num_kv_heads - 1) * kv_head_stride + rows * head_dim
+        if k_src.size < need_src or v_src.size < need_src:
+            raise ValueError("sources too small")
+        if k_cache.size < need_c or v_cache.size < need_c:
+            raise ValueError("caches too small")
+        rc = self.lib.oracle_kv_write(_ptr(k_src, _FP), _ptr(v_src, _FP), int(src_row_stride),
+                                      _ptr(k_cache, _FP), _ptr(v_cache, _FP), int(kv_head_stride),
+                                      int(ring_slots), T, start_pos, num_kv_heads, head_dim)
+        if rc != 0:
+            raise ValueError(f"oracle_kv_write returned {rc}")
 
 
 def _check_sizes(q, k, v, T, start_pos, num_heads, num_kv_heads, head_dim, qs, ks, ring_slots=0):

@@ -331,3 +331,39 @@ int oracle_row_probabilities(const float *q, int64_t q_row_stride,
     *first = first_key(pos, window);
     return pos - *first + 1;
 }
+
+/*
+ * KV cache write, the step before the attention: the gnosis page ("What
+ * already shipped", Phase A) stores every token's K and V in the cache before
+ * the attention runs; the TensorSharp page (section 4, requirement R4) puts
+ * position pos at row pos of a global layer's cache and at slot
+ * pos % (ring size) of a sliding-window layer's ring.  Tokens i = 0..T-1 are
+ * written in order: K of token i, kv head kh, element d is read from
+ * k_src[i*src_row_stride + kh*head_dim + d] (V alike) and stored at
+ * k_cache[kh*kv_head_stride + row*head_dim + d] with row = start_pos + i, or
+ * (start_pos + i) % ring_slots when ring_slots > 0.  Returns 0, or -1 for
+ * invalid arguments.
+ */
+int oracle_kv_write(const float *k_src, const float *v_src, int64_t src_row_stride,
+                    float *k_cache, float *v_cache, int64_t kv_head_stride, int ring_slots,
+                    int T, int start_pos, int num_kv_heads, int head_dim)
+{
+    if (!k_src || !v_src || !k_cache || !v_cache) return -1;
+    if (T < 1 || start_pos < 0 || num_kv_heads < 1 || head_dim < 1 || ring_slots < 0) return -1;
+    if (src_row_stride < (int64_t)num_kv_heads * head_dim) return -1;
+    const int64_t rows = ring_slots > 0 ? ring_slots : (int64_t)start_pos + T;
+    if (kv_head_stride < rows * head_dim) return -1;
+    for (int i = 0; i < T; ++i) {
+        const int64_t pos = (int64_t)start_pos + i;
+        const int64_t row = ring_slots > 0 ? pos % ring_slots : pos;
+        for (int kh = 0; kh < num_kv_heads; ++kh) {
+            const int64_t src = (int64_t)i * src_row_stride + (int64_t)kh * head_dim;
+            const int64_t dst = (int64_t)kh * kv_head_stride + row * head_dim;
+            for (int d = 0; d < head_dim; ++d) {
+                k_cache[dst + d] = k_src[src + d];
+                v_cache[dst + d] = v_src[src + d];
+            }
+        }
+    }
+    return 0;
+}

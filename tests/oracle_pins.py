@@ -24,6 +24,10 @@ when that build disagrees with what the pages or the mathematics fix:
                 page, section 4, requirement R4): the closed form above still
                 holds, and a chunk loop through the ring gives the rows of the
                 one-shot prefill over the linear cache, bit for bit
+  cache write   appended rows equal the source rows and nothing else moves;
+                a ring slot holds the last token written to it; writing each
+                chunk into a ring and then attending equals the one-shot
+                prefill
 
 The module is shared by ``test_oracle_pins.py`` (the real oracle must pass
 every pin) and ``test_oracle_mutants.py`` (each planted mistake must fail at
@@ -389,6 +393,65 @@ def pin_ring_chunked_equals_linear(orc):
         raise AssertionError("short ring accepted")
 
 
+def pin_kv_write_linear(orc):
+    """Appending a chunk writes rows start_pos .. start_pos+T-1 of every kv head
+    from the (strided) source and touches nothing else."""
+    rng = np.random.default_rng(RNG_SEED + 14)
+    KVH, D, T, sp, cap, srs = 3, 8, 6, 5, 20, 3 * 8 + 8
+    ks, vs = _rand(rng, (T, srs)), _rand(rng, (T, srs))
+    kc = np.full((KVH, cap, D), np.nan, np.float32)
+    vc = np.full((KVH, cap, D), np.nan, np.float32)
+    orc.kv_write(ks, vs, srs, kc, vc, cap * D, T, sp, KVH, D)
+    for kh in range(KVH):
+        assert np.array_equal(kc[kh, sp:sp + T], ks[:, kh * D:(kh + 1) * D])
+        assert np.array_equal(vc[kh, sp:sp + T], vs[:, kh * D:(kh + 1) * D])
+    assert np.isnan(kc[:, :sp]).all() and np.isnan(kc[:, sp + T:]).all()
+    assert np.isnan(vc[:, :sp]).all() and np.isnan(vc[:, sp + T:]).all()
+
+
+def pin_kv_write_ring(orc):
+    """In a ring of R slots each slot ends up holding the chunk's last token
+    whose position falls on it (in-order writes), or what it held before."""
+    rng = np.random.default_rng(RNG_SEED + 15)
+    KVH, D = 2, 4
+    for T, sp, R in ((11, 3, 4), (3, 9, 8), (8, 0, 8), (1, 29, 5)):
+        ks, vs = _rand(rng, (T, KVH * D)), _rand(rng, (T, KVH * D))
+        old = _rand(rng, (KVH, R, D))
+        kc, vc = old.copy(), old.copy()
+        orc.kv_write(ks, vs, KVH * D, kc, vc, R * D, T, sp, KVH, D, ring_slots=R)
+        for slot in range(R):
+            hits = [i for i in range(T) if (sp + i) % R == slot]
+            for kh in range(KVH):
+                want_k = ks[hits[-1], kh * D:(kh + 1) * D] if hits else old[kh, slot]
+                want_v = vs[hits[-1], kh * D:(kh + 1) * D] if hits else old[kh, slot]
+                assert np.array_equal(kc[kh, slot], want_k), (T, sp, R, slot)
+                assert np.array_equal(vc[kh, slot], want_v), (T, sp, R, slot)
+
+
+def pin_kv_write_then_attend(orc):
+    """Prefill as the pages run it, chunk by chunk: write the chunk's K/V into a
+    ring (then attend over it) equals the one-shot prefill over the whole
+    prompt's K/V, bit for bit."""
+    rng = np.random.default_rng(RNG_SEED + 16)
+    H, KVH, D, N, W = 4, 2, 8, 30, 5
+    q = _rand(rng, (N, H * D))
+    ksrc, vsrc = _rand(rng, (N, KVH * D)), _rand(rng, (N, KVH * D))
+    k_lin = np.ascontiguousarray(ksrc.reshape(N, KVH, D).transpose(1, 0, 2))
+    v_lin = np.ascontiguousarray(vsrc.reshape(N, KVH, D).transpose(1, 0, 2))
+    full = orc.attention(q, k_lin, v_lin, N, 0, H, KVH, D, window=W)
+    R = W + 9 - 1
+    kr = np.full((KVH, R, D), np.nan, np.float32)
+    vr = np.full((KVH, R, D), np.nan, np.float32)
+    start = 0
+    for T in (9, 1, 9, 4, 7):
+        orc.kv_write(ksrc[start:start + T], vsrc[start:start + T], KVH * D, kr, vr, R * D, T,
+                     start, KVH, D, ring_slots=R)
+        got = orc.attention(q[start:start + T], kr, vr, T, start, H, KVH, D, window=W,
+                            ring_slots=R)
+        assert np.array_equal(got, full[start:start + T]), start
+        start += T
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -405,4 +468,7 @@ ALL_PINS = [
     pin_strided_layouts,
     pin_ring_closed_form,
     pin_ring_chunked_equals_linear,
+    pin_kv_write_linear,
+    pin_kv_write_ring,
+    pin_kv_write_then_attend,
 ]

@@ -41,6 +41,11 @@ MUTANTS = [
     ("value_row_relative_to_lo", [("v_head + key_row(P, j) * D", "v_head + key_row(P, j - lo) * D", 1)]),
     ("ring_slot_off_by_one", [("return P->ring > 0 ? j % P->ring : j;",
                                "return P->ring > 0 ? (j + 1) % P->ring : j;", 1)]),
+    ("kv_write_slot_off_by_one", [("const int64_t row = ring_slots > 0 ? pos % ring_slots : pos;",
+                                   "const int64_t row = ring_slots > 0 ? (pos + 1) % ring_slots : pos;", 1)]),
+    ("kv_write_first_token_wins", [("for (int i = 0; i < T; ++i) {\n        const int64_t pos",
+                                    "for (int i = T - 1; i >= 0; --i) {\n        const int64_t pos", 1)]),
+    ("kv_write_v_from_k", [("v_cache[dst + d] = v_src[src + d];", "v_cache[dst + d] = k_src[src + d];", 1)]),
     ("ring_keys_of_value_slots", [("const float *k_row = k_head + key_row(P, j) * D;",
                                    "const float *k_row = k_head + (P->ring > 0 ? (j + P->ring - 1) % P->ring : j) * D;", 1)]),
     ("query_row_of_first_token", [("const int pos = P->start_pos + t;", "const int pos = P->start_pos;", 1)]),
