@@ -128,6 +128,83 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"copy_bytes": nbytes, "dispatches": 5}), flush=True)
 
 
+def kv_write_bench(args):
+    """The step before the attention: each chunk's K and V rows (one [T x KVH*D]
+    source each) stored in the workload's cache (rows start_pos+i, or ring slots).
+    Bytes = the rows read once and written once.  The kernels take a few
+    microseconds, less than a host launch, so the K timed steps are recorded
+    into one HIP graph on a side stream and replayed between two events."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU.", file=sys.stderr)
+        sys.exit(2)
+    lib = pa.load()
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[args.workload]
+    KVH, D = wl.num_kv_heads, wl.head_dim
+    eb = 4 if wl.dtype == "f32" else 2
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    rows = wl.ring or wl.capacity
+    k_cache = torch.zeros(KVH, rows, D, dtype=tdt, device=dev)
+    v_cache = torch.zeros_like(k_cache)
+    gen = torch.Generator(device=dev).manual_seed(wl.seed)
+    side = torch.cuda.Stream()
+    calls, keep, bytes_step = [], [], 0
+    for T, sp in wl.chunks:
+        ks = torch.randn(T, KVH * D, generator=gen, device=dev).to(tdt)
+        vs = torch.randn(T, KVH * D, generator=gen, device=dev).to(tdt)
+        calls.append((pa.binding.DTYPE_CODES[wl.dtype], ks.data_ptr(), vs.data_ptr(), KVH * D,
+                      k_cache.data_ptr(), v_cache.data_ptr(), rows * D, wl.ring, T, sp, KVH, D,
+                      side.cuda_stream))
+        keep.append((ks, vs))
+        bytes_step += 2 * 2 * min(T, wl.ring or T) * KVH * D * eb
+    fn = lib.prefill_kv_write
+    torch.cuda.synchronize()
+
+    def step():
+        for a in calls:
+            st = fn(*a)
+            if st != pa.PA_OK:
+                raise pa.PrefillAttnError(st, "prefill_kv_write")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    n_warm, t_w = 0, time.perf_counter()
+    with torch.cuda.stream(side):
+        while n_warm < max(1, args.warmup or 1) or (args.warmup is None and
+                                                      time.perf_counter() - t_w < WARMUP_S):
+            g.replay()
+            side.synchronize()
+            n_warm += 1
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(side)
+        g.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    print(f"kv write: {len(calls)} calls per step, {ms_step * 1e3:.2f} us per step on the stream "
+          f"({ms_step * 1e3 / len(calls):.2f} us per call)", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "KV cache write GB/s (K and V rows read once and written once)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": n_warm * args.steps, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "num_kv_heads": KVH, "head_dim": D,
+                   "chunks": [list(c) for c in wl.chunks], "ring_slots": wl.ring or None,
+                   "bytes_per_step": bytes_step, "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+                   "timing": "K steps replayed from one HIP graph between two events"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_GBS, 4), "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +215,9 @@ def main():
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-write", action="store_true",
+                    help="time the KV cache write of the workload's chunks (prefill_kv_write) "
+                         "instead of the attention; HBM-bound, priced against 8 TB/s")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times "
                          "(reference for the HBM byte counters) and exit")
@@ -146,6 +226,9 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
 
+    if args.kv_write:
+        kv_write_bench(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(each GPU would run its own shard of kv heads; see the design notes).",

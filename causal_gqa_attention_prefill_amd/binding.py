@@ -55,6 +55,8 @@ def load():
     lib.prefill_attn_ex.restype = I
     lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, P, SZ, P]
     lib.prefill_attn_ring_ex.restype = I
+    lib.prefill_kv_write.argtypes = [I, P, P, I64, P, P, I64, I, I, I, I, I, P]
+    lib.prefill_kv_write.restype = I
     lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.prefill_attn_workspace_bytes.restype = SZ
     lib.prefill_attn_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(I64), I]
@@ -69,7 +71,7 @@ def header_functions() -> list[str]:
     """Names of the functions include/prefill_attn.h declares."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(prefill_attn\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(prefill_\w+)\s*\(", text)))
 
 
 def strerror(status: int) -> str:
@@ -201,3 +203,24 @@ def prefill_attn_ring_ex(q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_s
     return PreparedCall(q, q_row_stride, k_ring, v_ring, kv_head_stride, out, out_row_stride, T,
                         start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream,
                         ring_slots=ring_slots)()
+
+
+def prefill_kv_write(k_src, v_src, src_row_stride, k_cache, v_cache, kv_head_stride, T, start_pos,
+                     num_kv_heads, head_dim, ring_slots=0, stream=None):
+    """Store the chunk's K/V rows in the cache: row start_pos + i, or slot
+    (start_pos + i) % ring_slots of a ring (ring_slots > 0)."""
+    dt = _dtype_of(k_src)
+    for t in (v_src, k_cache, v_cache):
+        if t.dtype != k_src.dtype:
+            raise TypeError("sources and caches must share one storage type")
+    rows = ring_slots if ring_slots else start_pos + T
+    _need(k_src, (T - 1) * src_row_stride + num_kv_heads * head_dim, "k_src")
+    _need(v_src, (T - 1) * src_row_stride + num_kv_heads * head_dim, "v_src")
+    _need(k_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "k_cache")
+    _need(v_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "v_cache")
+    st = load().prefill_kv_write(DTYPE_CODES[dt], k_src.data_ptr(), v_src.data_ptr(), src_row_stride,
+                                 k_cache.data_ptr(), v_cache.data_ptr(), kv_head_stride,
+                                 int(ring_slots), T, start_pos, num_kv_heads, head_dim,
+                                 _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st, "prefill_kv_write")

@@ -1281,6 +1281,38 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
                                 (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
 }
 
+// ---- KV cache write (companion kernel) -------------------------------------------------
+//
+// The step before the attention: each token of the chunk stores its K and V
+// rows in the cache (the gnosis page, "What already shipped", Phase A; the
+// TensorSharp page, section 4, requirement R4: global layers at row
+// start_pos + i, sliding-window layers at slot (start_pos + i) % ring).
+// Element e of the flat (token, kv head, 16-byte chunk) space of K, then of V,
+// is one thread's 16-byte move; consecutive threads read consecutive bytes of
+// a token's K (or V) block and write consecutive bytes of one cache row.  In a
+// ring, a token that a later token of the same chunk overwrites is not written
+// (only the last `ring` tokens are), which leaves what in-order writes leave.
+__global__ __launch_bounds__(256) void kv_write(const uint8_t *k_src, const uint8_t *v_src,
+                                                int64_t src_row_bytes, uint8_t *k_cache,
+                                                uint8_t *v_cache, int64_t head_bytes, int row_bytes,
+                                                int KVH, int t_first, int T, int start_pos, int ring) {
+    const int cpr = row_bytes / 16;                       // chunks per cache row
+    const int per_token = KVH * cpr;
+    const int n = (T - t_first) * per_token;              // chunks of K (and of V)
+    const int stride = (int)(gridDim.x * blockDim.x);
+    for (int idx = (int)(blockIdx.x * blockDim.x + threadIdx.x); idx < 2 * n; idx += stride) {
+        const bool is_v = idx >= n;
+        const int e = is_v ? idx - n : idx;
+        const int i = t_first + e / per_token;
+        const int c = e - (i - t_first) * per_token;      // chunk within the token's block
+        const int kh = c / cpr, cc = c - kh * cpr;
+        const int64_t pos = (int64_t)start_pos + i;
+        const int64_t slot = ring ? pos % ring : pos;
+        const u32x4 val = *(const u32x4 *)((is_v ? v_src : k_src) + i * src_row_bytes + (int64_t)c * 16);
+        *(u32x4 *)((is_v ? v_cache : k_cache) + kh * head_bytes + slot * row_bytes + (int64_t)cc * 16) = val;
+    }
+}
+
 // ---- host side -----------------------------------------------------------------------
 
 using KernelFn = void (*)(Params);
@@ -1657,6 +1689,36 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const v
     return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride,
                   ring_slots >= L ? 0 : ring_slots, out, out_row_stride, T, start_pos, num_heads,
                   num_kv_heads, head_dim, window, workspace, workspace_bytes, stream);
+}
+
+int prefill_kv_write(int dtype, const void *k_src, const void *v_src, int64_t src_row_stride,
+                     void *k_cache, void *v_cache, int64_t kv_head_stride, int ring_slots, int T,
+                     int start_pos, int num_kv_heads, int head_dim, void *stream) {
+    if (!k_src || !v_src || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+    if (T < 1 || start_pos < 0 || num_kv_heads < 1 || head_dim < 1 || ring_slots < 0)
+        return PA_ERR_INVALID_ARG;
+    if ((int64_t)start_pos + T > INT32_MAX) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_BF16 && dtype != PA_DTYPE_F16)
+        return PA_ERR_UNSUPPORTED;
+    const int64_t rows = ring_slots ? ring_slots : (int64_t)start_pos + T;
+    if (src_row_stride < (int64_t)num_kv_heads * head_dim) return PA_ERR_INVALID_ARG;
+    if (kv_head_stride < rows * head_dim) return PA_ERR_INVALID_ARG;
+    const int eb = elem_bytes(dtype);
+    const int64_t row_bytes = (int64_t)head_dim * eb;
+    if (row_bytes % 16 || (src_row_stride * eb) % 16 || (kv_head_stride * eb) % 16)
+        return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_UNSUPPORTED;
+    // tokens a later token of the chunk overwrites in a ring are skipped
+    const int t_first = ring_slots && T > ring_slots ? T - ring_slots : 0;
+    const int64_t chunks = 2 * (int64_t)(T - t_first) * num_kv_heads * (row_bytes / 16);
+    if (chunks > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(chunks, 256), 8 * kCus);
+    hipLaunchKernelGGL(kv_write, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint8_t *)k_src, (const uint8_t *)v_src, src_row_stride * eb,
+                       (uint8_t *)k_cache, (uint8_t *)v_cache, kv_head_stride * eb, (int)row_bytes,
+                       num_kv_heads, t_first, T, start_pos, ring_slots);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_heads,

@@ -136,6 +136,30 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride,
                          int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * KV cache write, the step before the attention (gnosis page, "What already
+ * shipped": Phase A stores each token's K/V in the cache; TensorSharp page,
+ * section 4, requirement R4: global layers append at row start_pos + i,
+ * sliding-window layers write slot (start_pos + i) % ring_slots).
+ *   source  K of token i, kv head kh: k_src[i*src_row_stride + kh*head_dim + d]
+ *           (V alike from v_src), i in 0..T-1; a fused QKV row passes
+ *           k_src = row + num_heads*head_dim, v_src = k_src + num_kv_heads*head_dim
+ *           and src_row_stride = (num_heads + 2*num_kv_heads)*head_dim
+ *   cache   ring_slots = 0: k_cache[kh*kv_head_stride + (start_pos+i)*head_dim + d]
+ *           (kv_head_stride >= (start_pos+T)*head_dim); ring_slots > 0: row
+ *           (start_pos+i) % ring_slots (kv_head_stride >= ring_slots*head_dim)
+ * The result is that of writing the tokens in order: in a ring shorter than
+ * the chunk, only the last ring_slots tokens land.  Nothing else in the
+ * cache is touched.  dtype is a PA_DTYPE_* value (the element type of source
+ * and cache alike); rows of head_dim elements must be a multiple of 16
+ * bytes, pointers and strides 16-byte aligned.  Sources and caches must not
+ * overlap.  Asynchronous on `stream`; arguments are checked first
+ * (PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED, nothing enqueued).
+ */
+int prefill_kv_write(int dtype, const void *k_src, const void *v_src, int64_t src_row_stride,
+                     void *k_cache, void *v_cache, int64_t kv_head_stride, int ring_slots,
+                     int T, int start_pos, int num_kv_heads, int head_dim, void *stream);
+
+/*
  * Scratch bytes prefill_attn_ex (or prefill_attn_ring_ex) needs for these
  * arguments (0: none).  Returns 0 as well for arguments that are invalid or
  * unsupported.

@@ -19,7 +19,7 @@ def test_exports_every_declared_function(lib):
     names = pa.header_functions()
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
                           "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
-                          "prefill_attn_plan", "prefill_attn_strerror"}
+                          "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -143,3 +143,25 @@ def test_ring_arguments(lib):
     assert call(2 ** 22, w=0, s=2 ** 22 - T) == U
     # every shape check of prefill_attn_ex applies too
     assert call(W + T - 1, t=0) == E
+
+
+def test_kv_write_arguments(lib):
+    """prefill_kv_write checks its arguments before anything is enqueued."""
+    kw = lib.prefill_kv_write
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    KVH, D, T, sp = 2, 64, 10, 100
+
+    def call(dtype=1, ks=FAKE, vs=FAKE, srs=KVH * D, kc=FAKE, vc=FAKE, kvs=None, ring=0, t=T, s=sp,
+             kvh=KVH, d=D):
+        kvs = ((ring or (s + t)) * d) if kvs is None else kvs
+        return kw(dtype, ks, vs, srs, kc, vc, kvs, ring, t, s, kvh, d, None)
+
+    assert call(ks=None) == E and call(vc=None) == E
+    assert call(t=0) == E and call(s=-1) == E and call(kvh=0) == E and call(ring=-1) == E
+    assert call(srs=KVH * D - 1) == E
+    assert call(kvs=(sp + T) * D - 8) == E
+    assert call(ring=16, kvs=16 * D - 8) == E
+    assert call(dtype=9) == U
+    assert call(d=4) == U                      # 8-byte rows
+    assert call(ks=FAKE + 8) == U              # misaligned
+    assert call(srs=KVH * D + 4) == U          # source rows not 16-byte multiples
