@@ -92,6 +92,13 @@ class Oracle:
             _INT, _INT, _INT, _INT, _INT, _INT, _INT]
         lib.oracle_prefill_attention_rows_ring.restype = _INT
         lib.oracle_kv_write.argtypes = [_FP, _FP, _I64, _FP, _FP, _I64, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_prefill_attention_paged.argtypes = [
+            _FP, _I64, _FP, _FP, _INT, _INT, _IP, _DP, _INT, _INT, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_prefill_attention_paged.restype = _INT
+        lib.oracle_prefill_attention_rows_paged.argtypes = [
+            _FP, _I64, _FP, _FP, _INT, _INT, _IP, _IP, _IP, _I64, _DP,
+            _INT, _INT, _INT, _INT, _INT, _INT, _INT]
+        lib.oracle_prefill_attention_rows_paged.restype = _INT
         lib.oracle_kv_write.restype = _INT
         self.lib = lib
 
@@ -163,6 +170,54 @@ class Oracle:
             raise ValueError(f"oracle_row_probabilities returned {n}")
         return first.value, probs[:n].copy()
 
+
+    def _pool_args(self, k_pool, v_pool, page_table, page_size, T, start_pos, num_heads, num_kv_heads,
+                   head_dim, q, qs):
+        k_pool, v_pool = _f32(k_pool), _f32(v_pool)
+        pt = np.ascontiguousarray(page_table, dtype=np.int32)
+        page_elems = page_size * num_kv_heads * head_dim
+        if k_pool.size % page_elems or v_pool.size != k_pool.size:
+            raise ValueError("pools must hold whole pages of page_size x num_kv_heads x head_dim")
+        if pt.size * page_size < start_pos + T:
+            raise ValueError("the page table does not cover the keys")
+        if q.size < (T - 1) * qs + num_heads * head_dim:
+            raise ValueError("q too small")
+        return k_pool, v_pool, pt, k_pool.size // page_elems
+
+    def attention_paged(self, q, k_pool, v_pool, page_table, page_size, T, start_pos, num_heads,
+                        num_kv_heads, head_dim, window=0, q_row_stride=None, nthreads=None):
+        """Whole chunk over a paged cache (pools of pages of page_size positions of
+        every kv head, key j in page page_table[j // page_size]); fp64 [T, H, D]."""
+        q = _f32(q)
+        qs = int(q_row_stride or num_heads * head_dim)
+        k_pool, v_pool, pt, npages = self._pool_args(k_pool, v_pool, page_table, page_size, T,
+                                                     start_pos, num_heads, num_kv_heads, head_dim, q, qs)
+        out = np.empty((T, num_heads, head_dim), dtype=np.float64)
+        rc = self.lib.oracle_prefill_attention_paged(
+            _ptr(q, _FP), qs, _ptr(k_pool, _FP), _ptr(v_pool, _FP), page_size, npages, _ptr(pt, _IP),
+            _ptr(out, _DP), T, start_pos, num_heads, num_kv_heads, head_dim, window,
+            nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_prefill_attention_paged returned {rc}")
+        return out
+
+    def rows_paged(self, q, k_pool, v_pool, page_table, page_size, T, start_pos, num_heads,
+                   num_kv_heads, head_dim, row_t, row_h, window=0, q_row_stride=None, nthreads=None):
+        """Rows (row_t[i], row_h[i]) over a paged cache; fp64 [len(row_t), D]."""
+        q = _f32(q)
+        qs = int(q_row_stride or num_heads * head_dim)
+        k_pool, v_pool, pt, npages = self._pool_args(k_pool, v_pool, page_table, page_size, T,
+                                                     start_pos, num_heads, num_kv_heads, head_dim, q, qs)
+        rt = np.ascontiguousarray(row_t, dtype=np.int32)
+        rh = np.ascontiguousarray(row_h, dtype=np.int32)
+        out = np.empty((rt.size, head_dim), dtype=np.float64)
+        rc = self.lib.oracle_prefill_attention_rows_paged(
+            _ptr(q, _FP), qs, _ptr(k_pool, _FP), _ptr(v_pool, _FP), page_size, npages, _ptr(pt, _IP),
+            _ptr(rt, _IP), _ptr(rh, _IP), rt.size, _ptr(out, _DP), T, start_pos, num_heads,
+            num_kv_heads, head_dim, window, nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_prefill_attention_rows_paged returned {rc}")
+        return out
 
     def kv_write(self, k_src, v_src, src_row_stride, k_cache, v_cache, kv_head_stride, T,
                  start_pos, num_kv_heads, head_dim, ring_slots=0):

@@ -47,6 +47,14 @@
  * min(L, window + T - 1) slots (L for window 0); a shorter ring is an invalid
  * argument.
  *
+ * Paged caches (the *_paged entry points; the FreeToken page "perf(spec):
+ * capture the gemma4 assistant draft in cuda graphs" reads a sequence's
+ * [0, cached_len) keys through its page table).  A pool of num_pages pages,
+ * each holding page_size consecutive positions of every kv head: element
+ * (pg, kh, r, d) at pool[((pg*num_kv_heads + kh)*page_size + r)*head_dim + d];
+ * key j of kv head kh is row j % page_size of page page_table[j / page_size].
+ * Every key a row reads must lie on a page of the pool (else invalid).
+ *
  * Inputs are fp32 storage.  bf16 and fp16 values widen exactly to fp32, so
  * callers holding those types pass their fp32 images.  Every product and sum
  * is done in fp64 (the page's "independent f64 CPU recompute",
@@ -72,7 +80,12 @@ struct problem {
     int64_t kv_head_stride; /* elements between consecutive kv heads      */
     int T, start_pos, num_heads, num_kv_heads, head_dim, window;
     int ring;               /* ring slots per kv head; 0: key j in row j */
+    const int32_t *page_table; /* paged cache: page of each page_size keys, else NULL */
+    int page_size, num_pages;
 };
+
+static int check_pages(const struct problem *P);
+static int first_key(int pos, int window);
 
 static int check_problem(const struct problem *P)
 {
@@ -83,6 +96,7 @@ static int check_problem(const struct problem *P)
     if (P->window < 0) return -1;
     if (P->q_row_stride < (int64_t)P->num_heads * P->head_dim) return -1;
     if (P->ring < 0) return -1;
+    if (P->page_table) return check_pages(P);
     const int64_t L = (int64_t)P->start_pos + P->T;
     if (P->ring > 0) {
         const int64_t need = P->window > 0 && (int64_t)P->window + P->T - 1 < L
@@ -99,6 +113,31 @@ static int check_problem(const struct problem *P)
 static int64_t key_row(const struct problem *P, int j)
 {
     return P->ring > 0 ? j % P->ring : j;
+}
+
+/* Element offset of key j of kv head kv_h from the start of k (or v). */
+static int64_t key_offset(const struct problem *P, int kv_h, int j)
+{
+    if (P->page_table) {
+        const int64_t page = P->page_table[j / P->page_size];
+        return ((page * P->num_kv_heads + kv_h) * P->page_size + j % P->page_size) * P->head_dim;
+    }
+    return (int64_t)kv_h * P->kv_head_stride + key_row(P, j) * P->head_dim;
+}
+
+/* Paged cache: every key some row reads lies on a page of the pool. */
+static int check_pages(const struct problem *P)
+{
+    if (P->page_size < 1 || P->num_pages < 1) return -1;
+    for (int t = 0; t < P->T; ++t) {
+        const int last = P->start_pos + t;
+        const int lo = first_key(last, P->window);
+        for (int j = lo; j < last + 1; ++j) {
+            const int32_t pg = P->page_table[j / P->page_size];
+            if (pg < 0 || pg >= P->num_pages) return -1;
+        }
+    }
+    return 0;
 }
 
 /* First valid key of the query at absolute position pos. */
@@ -120,14 +159,12 @@ static void attend_row(const struct problem *P, int t, int h, double *scores, do
     const int num_kv_groups = P->num_heads / P->num_kv_heads;
     const int kv_h = h / num_kv_groups;
     const float *q_row = P->q + (int64_t)t * P->q_row_stride + (int64_t)h * D;
-    const float *k_head = P->k + (int64_t)kv_h * P->kv_head_stride;
-    const float *v_head = P->v + (int64_t)kv_h * P->kv_head_stride;
     const double scale = 1.0 / sqrt((double)D);
     const int n = pos - lo + 1;
 
     /* scores over the valid keys lo..=pos, scaled before the softmax */
     for (int j = lo; j <= pos; ++j) {
-        const float *k_row = k_head + key_row(P, j) * D;
+        const float *k_row = P->k + key_offset(P, kv_h, j);
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
             dot += (double)q_row[d] * (double)k_row[d];
@@ -151,7 +188,7 @@ static void attend_row(const struct problem *P, int t, int h, double *scores, do
         out_row[d] = 0.0;
     for (int j = lo; j <= pos; ++j) {
         const double p = scores[j - lo];
-        const float *v_row = v_head + key_row(P, j) * D;
+        const float *v_row = P->v + key_offset(P, kv_h, j);
         for (int d = 0; d < D; ++d)
             out_row[d] += p * (double)v_row[d];
     }
@@ -253,7 +290,7 @@ int oracle_prefill_attention(const float *q, int64_t q_row_stride,
                              int head_dim, int window, int nthreads)
 {
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0, NULL, 0, 0};
     if (check_problem(&P) || !out) return -1;
     return run_rows(&P, NULL, NULL, (int64_t)T * num_heads, out, nthreads);
 }
@@ -266,7 +303,7 @@ int oracle_prefill_attention_ring(const float *q, int64_t q_row_stride,
                                   int nthreads)
 {
     struct problem P = {q, k_ring, v_ring, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots, NULL, 0, 0};
     if (ring_slots < 1 || check_problem(&P) || !out) return -1;
     return run_rows(&P, NULL, NULL, (int64_t)T * num_heads, out, nthreads);
 }
@@ -301,7 +338,7 @@ int oracle_prefill_attention_rows_ring(const float *q, int64_t q_row_stride,
                                        int num_kv_heads, int head_dim, int window, int nthreads)
 {
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, ring_slots, NULL, 0, 0};
     if (check_problem(&P) || !out || !row_t || !row_h || nrows < 1) return -1;
     for (int64_t i = 0; i < nrows; ++i)
         if (row_t[i] < 0 || row_t[i] >= T || row_h[i] < 0 || row_h[i] >= num_heads) return -1;
@@ -320,7 +357,7 @@ int oracle_row_probabilities(const float *q, int64_t q_row_stride,
                              int head_dim, int window)
 {
     struct problem P = {q, k_cache, v_cache, q_row_stride, kv_head_stride,
-                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0};
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0, NULL, 0, 0};
     if (check_problem(&P) || !probs || !first) return -1;
     if (t < 0 || t >= T || h < 0 || h >= num_heads) return -1;
     double *out_row = (double *)malloc(sizeof(double) * (size_t)head_dim);
@@ -366,4 +403,40 @@ int oracle_kv_write(const float *k_src, const float *v_src, int64_t src_row_stri
         }
     }
     return 0;
+}
+
+/*
+ * Selected rows (row_t[i], row_h[i]) over a paged cache (pools k_pool and
+ * v_pool of num_pages pages of page_size positions): out is [nrows][head_dim].
+ * Returns 0, -1 for invalid arguments (a key some row reads off the pool
+ * included), -2 when memory runs out.
+ */
+int oracle_prefill_attention_rows_paged(const float *q, int64_t q_row_stride,
+                                        const float *k_pool, const float *v_pool, int page_size,
+                                        int num_pages, const int32_t *page_table,
+                                        const int32_t *row_t, const int32_t *row_h, int64_t nrows,
+                                        double *out, int T, int start_pos, int num_heads,
+                                        int num_kv_heads, int head_dim, int window, int nthreads)
+{
+    struct problem P = {q, k_pool, v_pool, q_row_stride, 0,
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0,
+                        page_table, page_size, num_pages};
+    if (!page_table || check_problem(&P) || !out || !row_t || !row_h || nrows < 1) return -1;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (row_t[i] < 0 || row_t[i] >= T || row_h[i] < 0 || row_h[i] >= num_heads) return -1;
+    return run_rows(&P, row_t, row_h, nrows, out, nthreads);
+}
+
+/* Whole chunk over a paged cache: out is [T][num_heads][head_dim]. */
+int oracle_prefill_attention_paged(const float *q, int64_t q_row_stride,
+                                   const float *k_pool, const float *v_pool, int page_size,
+                                   int num_pages, const int32_t *page_table, double *out, int T,
+                                   int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                                   int window, int nthreads)
+{
+    struct problem P = {q, k_pool, v_pool, q_row_stride, 0,
+                        T, start_pos, num_heads, num_kv_heads, head_dim, window, 0,
+                        page_table, page_size, num_pages};
+    if (!page_table || check_problem(&P) || !out) return -1;
+    return run_rows(&P, NULL, NULL, (int64_t)T * num_heads, out, nthreads);
 }

@@ -28,6 +28,8 @@ when that build disagrees with what the pages or the mathematics fix:
                 a ring slot holds the last token written to it; writing each
                 chunk into a ring and then attending equals the one-shot
                 prefill
+  paged cache   pages in scrambled pool order give the linear result bit for
+                bit; the closed form above holds through pages
 
 The module is shared by ``test_oracle_pins.py`` (the real oracle must pass
 every pin) and ``test_oracle_mutants.py`` (each planted mistake must fail at
@@ -452,6 +454,78 @@ def pin_kv_write_then_attend(orc):
         start += T
 
 
+def _pages(rows, page_size, L, num_pages, order):
+    """Pool [num_pages, KVH, page_size, D] (NaN where no key sits) and table:
+    block b of keys goes to page order[b]."""
+    kvh, _, d = rows.shape
+    pool = np.full((num_pages, kvh, page_size, d), np.nan, np.float32)
+    n = -(-L // page_size)
+    for b in range(n):
+        for r in range(page_size):
+            j = b * page_size + r
+            if j < L:
+                pool[order[b], :, r] = rows[:, j]
+    return pool, np.array(order[:n], np.int32)
+
+
+def pin_paged_equals_linear(orc):
+    """A paged cache (pages in scrambled pool order, NaN in unused pool rows)
+    gives the linear cache's result bit for bit, with and without a window;
+    blocks below every row's window may point anywhere, even off the pool."""
+    rng = np.random.default_rng(RNG_SEED + 17)
+    H, KVH, D = 4, 2, 8
+    for T, sp, W, P in ((5, 40, 0, 8), (9, 30, 7, 4), (1, 63, 16, 16), (12, 0, 0, 4)):
+        L = sp + T
+        q, k, v = _case(rng, H, KVH, D, T, sp)
+        want = orc.attention(q, k, v, T, sp, H, KVH, D, window=W)
+        npages = -(-L // P) + 3
+        order = list(rng.permutation(npages))
+        kp, table = _pages(k, P, L, npages, order)
+        vp, _ = _pages(v, P, L, npages, order)
+        if W:
+            lo_min = max(0, sp - W + 1)
+            table = table.copy()
+            table[:lo_min // P] = -5            # blocks no row reads
+        got = orc.attention_paged(q, kp, vp, table, P, T, sp, H, KVH, D, window=W)
+        assert np.array_equal(got, want), (T, sp, W, P)
+        rt, rh = np.array([T - 1, 0]), np.array([0, H - 1])
+        sub = orc.rows_paged(q, kp, vp, table, P, T, sp, H, KVH, D, rt, rh, window=W)
+        assert np.array_equal(sub, want[rt, rh])
+    # a key some row reads whose page is off the pool is refused
+    q, k, v = _case(rng, H, KVH, D, 3, 5)
+    kp, table = _pages(k, 4, 8, 2, [1, 0])
+    vp, _ = _pages(v, 4, 8, 2, [1, 0])
+    bad = table.copy()
+    bad[1] = 7
+    try:
+        orc.attention_paged(q, kp, vp, bad, 4, 3, 5, H, KVH, D)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("page off the pool accepted")
+
+
+def pin_paged_closed_form(orc):
+    """q = 0 over a paged cache with V[kh, j] = j + 1000*kh: (lo + pos)/2 + 1000*kv_head(h)."""
+    H, KVH, D, T, sp, W, P = 4, 2, 4, 6, 37, 9, 8
+    L, G = sp + T, H // KVH
+    rng = np.random.default_rng(RNG_SEED + 18)
+    k = _rand(rng, (KVH, L, D))
+    v = np.empty((KVH, L, D), np.float32)
+    for kh in range(KVH):
+        v[kh] = (np.arange(L)[:, None] + 1000.0 * kh).astype(np.float32)
+    order = [3, 0, 5, 1, 4, 2, 6]
+    kp, table = _pages(k, P, L, 7, order)
+    vp, _ = _pages(v, P, L, 7, order)
+    out = orc.attention_paged(np.zeros((T, H * D), np.float32), kp, vp, table, P, T, sp, H, KVH, D,
+                              window=W)
+    for t in range(T):
+        pos = sp + t
+        lo = max(0, pos - W + 1)
+        for h in range(H):
+            assert np.abs(out[t, h] - ((lo + pos) / 2.0 + 1000.0 * (h // G))).max() <= 1e-9
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -471,4 +545,6 @@ ALL_PINS = [
     pin_kv_write_linear,
     pin_kv_write_ring,
     pin_kv_write_then_attend,
+    pin_paged_equals_linear,
+    pin_paged_closed_form,
 ]

@@ -34,11 +34,12 @@ MUTANTS = [
     ("dot_drops_first_dim", [("for (int d = 0; d < D; ++d)\n            dot +=",
                               "for (int d = 1; d < D; ++d)\n            dot +=", 1)]),
     ("q_stride_ignored", [("(int64_t)t * P->q_row_stride", "(int64_t)t * P->num_heads * D", 1)]),
-    ("v_head_stride_packed", [("P->v + (int64_t)kv_h * P->kv_head_stride",
-                               "P->v + (int64_t)kv_h * (P->start_pos + P->T) * D", 1)]),
+    ("v_head_stride_packed", [("const float *v_row = P->v + key_offset(P, kv_h, j);",
+                               "const float *v_row = P->v + key_offset(P, kv_h, j) - (int64_t)kv_h * "
+                               "P->kv_head_stride + (P->page_table ? 0 : (int64_t)kv_h * (P->start_pos + P->T) * D);", 1)]),
     ("softmax_denominator_off", [("scores[i] = scores[i] / total;",
                                   "scores[i] = scores[i] / (total + 1e-3);", 1)]),
-    ("value_row_relative_to_lo", [("v_head + key_row(P, j) * D", "v_head + key_row(P, j - lo) * D", 1)]),
+    ("value_row_relative_to_lo", [("P->v + key_offset(P, kv_h, j);", "P->v + key_offset(P, kv_h, j - lo);", 1)]),
     ("ring_slot_off_by_one", [("return P->ring > 0 ? j % P->ring : j;",
                                "return P->ring > 0 ? (j + 1) % P->ring : j;", 1)]),
     ("kv_write_slot_off_by_one", [("const int64_t row = ring_slots > 0 ? pos % ring_slots : pos;",
@@ -46,8 +47,11 @@ MUTANTS = [
     ("kv_write_first_token_wins", [("for (int i = 0; i < T; ++i) {\n        const int64_t pos",
                                     "for (int i = T - 1; i >= 0; --i) {\n        const int64_t pos", 1)]),
     ("kv_write_v_from_k", [("v_cache[dst + d] = v_src[src + d];", "v_cache[dst + d] = k_src[src + d];", 1)]),
-    ("ring_keys_of_value_slots", [("const float *k_row = k_head + key_row(P, j) * D;",
-                                   "const float *k_row = k_head + (P->ring > 0 ? (j + P->ring - 1) % P->ring : j) * D;", 1)]),
+    ("ring_keys_of_value_slots", [("const float *k_row = P->k + key_offset(P, kv_h, j);",
+                                   "const float *k_row = P->k + key_offset(P, kv_h, P->ring > 0 ? j + P->ring - 1 : j);", 1)]),
+    ("paged_row_off_by_one", [("+ j % P->page_size) * P->head_dim;", "+ (j + 1) % P->page_size) * P->head_dim;", 1)]),
+    ("paged_pool_head_major", [("((page * P->num_kv_heads + kv_h) * P->page_size",
+                                "(((int64_t)kv_h * P->num_pages + page) * P->page_size", 1)]),
     ("query_row_of_first_token", [("const int pos = P->start_pos + t;", "const int pos = P->start_pos;", 1)]),
 ]
 

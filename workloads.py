@@ -96,6 +96,24 @@ def ring_cache(rows: np.ndarray, ring_slots: int, L: int, fill) -> np.ndarray:
     return ring
 
 
+def paged_cache(rows: np.ndarray, page_size: int, L: int, num_pages: int, seed: int, fill):
+    """A paged cache holding keys 0 .. L-1 of ``rows`` ([kv heads, positions,
+    head_dim]): a pool of ``num_pages`` pages ([num_pages, kv heads, page_size,
+    head_dim]), the sequence's pages drawn in a seeded random order from the
+    pool, and its page table (int32, one entry per page_size keys).  Pool rows
+    that hold no key of the sequence hold ``fill``."""
+    kvh, _, d = rows.shape
+    n = (L + page_size - 1) // page_size
+    if n > num_pages:
+        raise ValueError("pool too small")
+    table = np.random.default_rng(seed).permutation(num_pages)[:n].astype(np.int32)
+    pool = np.full((num_pages, kvh, page_size, d), fill, dtype=rows.dtype)
+    for b in range(n):
+        j0, j1 = b * page_size, min(L, (b + 1) * page_size)
+        pool[table[b], :, :j1 - j0] = rows[:, j0:j1]
+    return pool, table
+
+
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even (finite inputs)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
