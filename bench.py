@@ -37,6 +37,7 @@ METRIC = "prefill attention TFLOP/s and % of MI355X bf16 MFMA peak (T=2048 chunk
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_GBS = 8000.0
 WARMUP_S = 0.3
+RIDGE_FLOP_PER_BYTE = 2516.6e12 / 8e12   # bf16 MFMA peak over HBM bandwidth
 KERNEL_SOURCE = os.path.join(ROOT, "causal_gqa_attention_prefill_amd", "csrc", "prefill_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -251,6 +252,7 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
         return t.view(torch.bfloat16 if wl.dtype == "bf16" else torch.float16)
 
+    page_kw = {}
     if wl.ring:
         # the cache as a ring of wl.ring slots per kv head (key j in slot j % ring),
         # as left by writing the keys up to the chunk's last one
@@ -259,6 +261,16 @@ def main():
         k = dev_tensor(workloads.ring_cache(x.k_store, wl.ring, L, 0))
         v = dev_tensor(workloads.ring_cache(x.v_store, wl.ring, L, 0))
         kv_stride, ring_slots = wl.ring * D, wl.ring
+    elif wl.page_size:
+        # the cache as a pool of pages in scrambled order plus the sequence's page table
+        assert len(wl.chunks) == 1
+        L = wl.chunks[0][1] + wl.chunks[0][0]
+        npages = -(-L // wl.page_size) + 16
+        kp, table = workloads.paged_cache(x.k_store, wl.page_size, L, npages, wl.seed, 0)
+        vp, _ = workloads.paged_cache(x.v_store, wl.page_size, L, npages, wl.seed, 0)
+        k, v = dev_tensor(kp), dev_tensor(vp)
+        kv_stride, ring_slots = 0, None
+        page_kw = {"page_table": torch.from_numpy(table).to(dev), "page_size": wl.page_size}
     else:
         k = dev_tensor(x.k_store)
         v = dev_tensor(x.v_store)
@@ -273,7 +285,7 @@ def main():
         nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
         ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
-                                     workspace=ws, ring_slots=ring_slots))
+                                     workspace=ws, ring_slots=ring_slots, **page_kw))
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -367,6 +379,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }
+    if flops_step / bytes_step < RIDGE_FLOP_PER_BYTE:
+        # below the ridge (short chunks over long caches): priced against HBM
+        gbs = bytes_step / len(calls) / (mean_launch_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS,
+                              "unit": "GB/s", "frac": round(gbs / HBM_GBS, 4), "traffic": traffic}
+    if wl.ring:
+        result["config"]["ring_slots"] = wl.ring
+    if wl.page_size:
+        result["config"]["page_size"] = wl.page_size
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)

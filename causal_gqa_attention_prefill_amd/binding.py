@@ -56,6 +56,9 @@ def load():
     lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, P, SZ, P]
     lib.prefill_attn_ring_ex.restype = I
     lib.prefill_kv_write.argtypes = [I, P, P, I64, P, P, I64, I, I, I, I, I, P]
+    lib.prefill_attn_paged_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, I, I, I, I, I, P, SZ,
+                                          P]
+    lib.prefill_attn_paged_ex.restype = I
     lib.prefill_kv_write.restype = I
     lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.prefill_attn_workspace_bytes.restype = SZ
@@ -157,14 +160,24 @@ class PreparedCall:
 
     def __init__(self, q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                  start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
-                 stream=None, ring_slots=None):
+                 stream=None, ring_slots=None, page_table=None, page_size=None):
         dt = _dtype_of(q)
         if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
             raise TypeError("q, k_cache and v_cache must share one storage type")
         rows = start_pos + T if ring_slots is None else ring_slots
         _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
-        _need(k_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "k_cache")
-        _need(v_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "v_cache")
+        if page_table is None:
+            _need(k_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "k_cache")
+            _need(v_cache, (num_kv_heads - 1) * kv_head_stride + rows * head_dim, "v_cache")
+        else:
+            # pools of whole pages; the table covers the call's keys
+            page_elems = page_size * num_kv_heads * head_dim
+            _need(k_cache, page_elems, "k_pool")
+            _need(v_cache, k_cache.numel(), "v_pool")
+            import torch
+            if page_table.dtype != torch.int32:
+                raise TypeError("page_table must be int32")
+            _need(page_table, -(-(start_pos + T) // page_size), "page_table")
         _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
         ws_ptr, ws_bytes = None, 0
         if workspace is not None:
@@ -173,12 +186,18 @@ class PreparedCall:
                 v_cache.data_ptr(), kv_head_stride)
         tail = (out.data_ptr(), out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim,
                 window, ws_ptr, ws_bytes, _stream(stream))
-        if ring_slots is None:
+        if page_table is not None:
+            self._name, self._fn = "prefill_attn_paged_ex", load().prefill_attn_paged_ex
+            self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                          v_cache.data_ptr(), int(page_size),
+                          k_cache.numel() // (page_size * num_kv_heads * head_dim),
+                          page_table.data_ptr()) + tail
+        elif ring_slots is None:
             self._name, self._fn, self._args = "prefill_attn_ex", load().prefill_attn_ex, head + tail
         else:
             self._name, self._fn = "prefill_attn_ring_ex", load().prefill_attn_ring_ex
             self._args = head + (int(ring_slots),) + tail
-        self._keep = (q, k_cache, v_cache, out, workspace)
+        self._keep = (q, k_cache, v_cache, out, workspace, page_table)
         self.out = out
 
     def __call__(self):
@@ -203,6 +222,17 @@ def prefill_attn_ring_ex(q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_s
     return PreparedCall(q, q_row_stride, k_ring, v_ring, kv_head_stride, out, out_row_stride, T,
                         start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream,
                         ring_slots=ring_slots)()
+
+
+def prefill_attn_paged_ex(q, q_row_stride, k_pool, v_pool, page_size, page_table, out,
+                          out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window=0,
+                          workspace=None, stream=None):
+    """Strided call over a paged cache: pools of pages of page_size positions of
+    every kv head (num_pages = pool elements / (page_size*num_kv_heads*head_dim)),
+    key j in page page_table[j // page_size] (int32 device tensor)."""
+    return PreparedCall(q, q_row_stride, k_pool, v_pool, 0, out, out_row_stride, T, start_pos,
+                        num_heads, num_kv_heads, head_dim, window, workspace, stream,
+                        page_table=page_table, page_size=page_size)()
 
 
 def prefill_kv_write(k_src, v_src, src_row_stride, k_cache, v_cache, kv_head_stride, T, start_pos,

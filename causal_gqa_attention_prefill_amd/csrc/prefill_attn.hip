@@ -91,10 +91,30 @@ struct Params {
     int kv_bytes;     // bytes of the L valid rows (linear) or of the ring slots of one kv head
     int L;            // keys of the call: start_pos + T
     int ring;         // ring cache: key j sits in slot j % ring of its kv head; 0: row j
+    const int32_t *page_table;  // paged cache: page of each block of 2^page_shift keys (else null)
+    int page_shift, num_pages;
     const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
     int vop_kt_lo;         // first KV tile held in vop
     int vop_tiles;         // KV tiles per kv head held in vop
 };
+
+// K/V cache layouts: key j of kv head kh is row j of the head's block
+// (linear), slot j % ring of it (ring, sliding-window layers), or row
+// j % page_size of page page_table[j / page_size] of a pool shared by the
+// kv heads (paged): element (pg, kh, r, d) at pool[((pg*KVH + kh)*page_size + r)*D + d].
+constexpr int kLinear = 0, kRing = 1, kPaged = 2;
+
+// Element offset of row (kh, key j) of a cache in any layout, or -1 when a
+// paged cache's entry for j lies outside the pool (such rows read as zero).
+template <int D>
+__device__ inline int64_t kv_row(const Params &p, int kh, int j) {
+    if (p.page_table) {
+        const int pg = p.page_table[j >> p.page_shift];
+        if (pg < 0 || pg >= p.num_pages) return -1;
+        return ((((int64_t)pg * p.KVH + kh) << p.page_shift) + (j & ((1 << p.page_shift) - 1))) * D;
+    }
+    return (int64_t)kh * p.kv_head_stride + (int64_t)(p.ring ? j % p.ring : j) * D;
+}
 
 // ---- storage types ---------------------------------------------------------
 
@@ -336,6 +356,28 @@ __device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_byte
     return 0;
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Paged cache: the K/V descriptors of the tile whose first key is j0 (a page
+// holds whole tiles), based at kv head kvh's rows of page `page` and covering
+// the page's rows below L, so rows at keys >= L read as zero; an entry outside
+// the pool reads as zeros.  soff = the tile's first row within the page.
+__device__ inline void paged_rsrc(const Params &p, int kvh, int j0, int row_bytes, int page,
+                                  __amdgpu_buffer_rsrc_t &rk, __amdgpu_buffer_rsrc_t &rv, int &soff) {
+    const int r0 = j0 & ((1 << p.page_shift) - 1);
+    const bool ok = page >= 0 && page < p.num_pages;
+    const int rows = ok ? min(1 << p.page_shift, p.L - (j0 - r0)) : 0;
+    const int64_t base = ok ? ((((int64_t)page * p.KVH + kvh) << p.page_shift) * row_bytes) : 0;
+    rk = head_rsrc((const uint8_t *)p.k + base, rows * row_bytes);
+    rv = head_rsrc((const uint8_t *)p.v + base, rows * row_bytes);
+    soff = r0 * row_bytes;
+}
+
+// The page of the tile whose first key is j (paged caches), -1 past L.
+__device__ inline int page_of(const Params &p, int j) {
+    return j < p.L ? p.page_table[j >> p.page_shift] : -1;
+}
+#endif
+
 // LDS operand reads issued as inline assembly.  The wait-count pass treats
 // the builtin transposed read as one that may alias any LDS DMA still in
 // flight and puts a vmcnt(0) in front of it, which would stall every P.V
@@ -443,21 +485,20 @@ struct Ones {
 //        (l%16, l/16), element e: key 32*step + 16*(e/4) + 4*(l/16) + e%4,
 //        d = 16*block + l%16
 template <int D, int BK, bool M16>
-__global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_t kv_head_stride,
-                                                       int L, int ring, int kt_lo, int ntiles,
-                                                       uint16_t *vop) {
+__global__ __launch_bounds__(256) void pack_v_operands(Params p, uint16_t *vop) {
+    const uint16_t *v = (const uint16_t *)p.v;
+    const int L = p.L, kt_lo = p.vop_kt_lo, ntiles = p.vop_tiles;
     constexpr int PITCH = D + 2;               // LDS row pitch (elements): column reads spread banks
     constexpr int CHUNKS = BK * D / 8;
     __shared__ uint32_t t32[BK * PITCH / 2];
     const uint16_t *t16 = (const uint16_t *)t32;
     const int tile = blockIdx.x, kvh = blockIdx.y;
     const int j0 = (kt_lo + tile) * BK;
-    const uint16_t *src = v + (int64_t)kvh * kv_head_stride;
     for (int cidx = threadIdx.x; cidx < CHUNKS; cidx += 256) {
         const int key = cidx / (D / 8), c8 = cidx % (D / 8);
         const int j = j0 + key;
-        const int64_t slot = ring ? j % ring : j;      // ring cache: key j in slot j % ring
-        const u32x4 val = j < L ? *(const u32x4 *)(src + slot * D + 8 * c8) : u32x4{0, 0, 0, 0};
+        const int64_t src = j < L ? kv_row<D>(p, kvh, j) : -1;   // any cache layout
+        const u32x4 val = src >= 0 ? *(const u32x4 *)(v + src + 8 * c8) : u32x4{0, 0, 0, 0};
         uint32_t *row = t32 + (key * PITCH + 8 * c8) / 2;
         row[0] = val[0];
         row[1] = val[1];
@@ -490,7 +531,7 @@ __global__ __launch_bounds__(256) void pack_v_operands(const uint16_t *v, int64_
     }
 }
 
-template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD, bool RING>
+template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD, int LAYOUT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -571,8 +612,9 @@ void attn_fwd16(Params p) {
     float lsum = 0.f;                // this lane's share of the row sum
     const float c = p.c;
 
+    int pg_next = -1;   // paged caches: page of the next tile this wave issues
     auto issue = [&](int kt, int kdst, int vdst) {
-        if constexpr (!RING) {
+        if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
@@ -581,6 +623,18 @@ void attn_fwd16(Params p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
             }
+        } else if constexpr (LAYOUT == kPaged) {
+            __amdgpu_buffer_rsrc_t pk, pv;
+            int soff;
+            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, pk, pv, soff);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    pk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    pv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], soff, 0, 0);
+            }
+            pg_next = page_of(p, (kt + 1) * BK);     // one tile ahead of its use
         } else {
             int ko[LOADS], vo[LOADS];
             const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
@@ -692,6 +746,7 @@ void attn_fwd16(Params p) {
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
     if (kb0 < ke) {
+        if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
         issue(kb0, B0K::value, B0V::value);
         wait_vmem();
         __syncthreads();
@@ -763,7 +818,7 @@ __device__ inline int swz_v16(int row) {
     return 2 * (row & 7);
 }
 
-template <class Ty, int D, int BK, bool VPACK, int KSPLIT, bool RING>
+template <class Ty, int D, int BK, bool VPACK, int KSPLIT, int LAYOUT>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -853,8 +908,9 @@ void attn_fwd16_r16(Params p) {
     float mref = -INFINITY, lsum = 0.f;
     const float c = p.c;
 
+    int pg_next = -1;   // paged caches: page of the next tile this wave issues
     auto issue = [&](int kt, int kdst, int vdst) {
-        if constexpr (!RING) {
+        if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
             const int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : base;
 #pragma unroll
@@ -864,6 +920,24 @@ void attn_fwd16_r16(Params p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
             }
+        } else if constexpr (LAYOUT == kPaged) {
+            // the operand-ordered V copy is linear in the call's tiles
+            __amdgpu_buffer_rsrc_t pk, pv;
+            int soff;
+            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, pk, pv, soff);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    pk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], soff, 0, 0);
+                if constexpr (VPACK)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i],
+                        (kt - p.vop_kt_lo) * TILE_BYTES, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        pv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], soff, 0, 0);
+            }
+            pg_next = page_of(p, (kt + 1) * BK);     // one tile ahead of its use
         } else {
             // the operand-ordered V copy is linear in the call's tiles; K (and
             // V read in place) come from the ring slots
@@ -992,6 +1066,7 @@ void attn_fwd16_r16(Params p) {
     const int kb0 = w.kt_begin, ke = w.kt_end;
     if constexpr (KSPLIT == 1) {
         if (kb0 < ke) {
+            if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
             issue(kb0, B0K::value, B0V::value);
             wait_vmem();
             __syncthreads();
@@ -1015,6 +1090,7 @@ void attn_fwd16_r16(Params p) {
         const int hb = half == 1 ? kb0 + niter : kb0;
         const int he = half == 0 ? kb0 + niter : ke;
         if (niter > 0) {
+            if constexpr (LAYOUT == kPaged) pg_next = hb < he ? page_of(p, hb * BK) : -1;
             if (hb < he) issue(hb, B0K::value, B0V::value);
             wait_vmem();
             __syncthreads();
@@ -1115,8 +1191,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
     const Tile w = locate<BK>(p);
     const Rows r = rows_of(p, w, wave, l32);
     const int L = p.start_pos + p.T;
-    const float *kbase = (const float *)p.k + (int64_t)w.kvh * p.kv_head_stride;
-    const float *vbase = (const float *)p.v + (int64_t)w.kvh * p.kv_head_stride;
 
     float qreg[HALF];
     {
@@ -1146,8 +1220,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
             const int idx = tid + i * kThreads;
             const int key = idx / (D / 4), c4 = idx % (D / 4);
             const int j = j0 + key;
-            const int64_t jr = p.ring ? j % p.ring : j;   // ring cache: key j in slot j % ring
-            kbuf[i] = j < L ? *(const f32x4 *)(kbase + jr * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int64_t row = j < L ? kv_row<D>(p, w.kvh, j) : -1;   // any cache layout
+            kbuf[i] = row >= 0 ? *(const f32x4 *)((const float *)p.k + row + 4 * c4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -1157,9 +1232,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + 4 * kq + u;
-                const int64_t jr = p.ring ? j % p.ring : j;
-                vbuf[i][u] = j < L ? *(const f32x4 *)(vbase + jr * D + 4 * c4)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int64_t row = j < L ? kv_row<D>(p, w.kvh, j) : -1;
+                vbuf[i][u] = row >= 0 ? *(const f32x4 *)((const float *)p.v + row + 4 * c4)
+                                      : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     };
@@ -1281,6 +1356,66 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
                                 (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
 }
 
+// The same merge for many splits (short chunks over long caches): one
+// work-group per (token, head) row, so that the splits are read in parallel
+// rather than one after another by each thread.  Threads s < S weigh split s
+// (after a work-group maximum of the m_s); then thread (g, d4) sums the
+// splits s = g mod NG of column block d4 and the NG partial sums are added in
+// LDS.
+template <int D>
+__global__ __launch_bounds__(512) void merge_splits_wide(const float *ws_o, const float2 *ws_ml,
+                                                         float *out, int64_t out_row_stride, int T,
+                                                         int H, int S) {
+    constexpr int C4 = D / 4, NG = 512 / C4;
+    __shared__ float wts[512];
+    __shared__ float red[512 / kWave];
+    __shared__ f32x4 part[512];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rows = (int64_t)T * H, row = blockIdx.x;
+    float2 ml = {-INFINITY, 0.f};
+    if (tid < S) ml = ws_ml[tid * rows + row];
+    // m* over the splits that saw a valid key
+    float m = ml.y > 0.f ? ml.x : -INFINITY;
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    float mstar = red[0];
+    for (int i = 1; i < 512 / kWave; ++i) mstar = fmaxf(mstar, red[i]);
+    const float wgt = ml.y > 0.f ? ml.y * __builtin_amdgcn_exp2f(ml.x - mstar) : 0.f;
+    wts[tid] = wgt;
+    __syncthreads();
+    float wsum = 0.f;
+    for (int i = 0; i < S; ++i) wsum += wts[i];
+    const int g = tid / C4, d4 = tid % C4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // eight splits' loads in flight per step (a split without a valid key for
+    // this row has weight 0 and its partial row is never added)
+    constexpr int U = 8;
+    for (int s0 = g; s0 < S; s0 += U * NG) {
+        f32x4 vals[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = s0 + u * NG;
+            vals[u] = sp < S ? *(const f32x4 *)(ws_o + (sp * rows + row) * D + 4 * d4)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int sp = s0 + u * NG;
+            const float w = sp < S ? wts[sp] : 0.f;
+            if (w > 0.f) acc += w * vals[u];
+        }
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (g == 0) {
+        for (int i = 1; i < NG; ++i) acc += part[i * C4 + d4];
+        const int t = (int)(row / H), h = (int)(row % H);
+        __builtin_nontemporal_store(acc * (1.f / wsum),
+                                    (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
+    }
+}
+
 // ---- KV cache write (companion kernel) -------------------------------------------------
 //
 // The step before the attention: each token of the chunk stores its K and V
@@ -1316,39 +1451,58 @@ __global__ __launch_bounds__(256) void kv_write(const uint8_t *k_src, const uint
 // ---- host side -----------------------------------------------------------------------
 
 using KernelFn = void (*)(Params);
-using PackFn = void (*)(const uint16_t *, int64_t, int, int, int, int, uint16_t *);
+using PackFn = void (*)(Params, uint16_t *);
 
 struct Variant {
     int dtype, D, BK;
     int groups_per_cu;         // resident work-groups per CU the kernel is sized for
     int threads;               // work-group size (4 or 8 wavefronts)
     int rows;                  // (token, head) rows per work-group
-    int ksplit;                // 2: the tile's keys are split between two wavefront halves
+    int ksplit;                // 2: the tile's keys are split between two wavefront halves;
+                               // 0: variant without the V operand-order copy, for few query tiles
     KernelFn fn;               // linear caches
     KernelFn fn_ring;          // ring caches (key j in slot j % ring)
+    KernelFn fn_paged;         // paged caches (key j in page page_table[j / page_size])
     PackFn pack;               // V operand-order pass (16-bit inputs), else null
 };
 
 const Variant kVariants[] = {
-    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2, false>, attn_fwd16<Bf16, 32, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2, false>, attn_fwd16<Bf16, 64, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2, false>, attn_fwd16<Bf16, 128, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1, false>, attn_fwd16_r16<Bf16, 256, 64, false, 1, true>, nullptr},
-    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2, false>, attn_fwd16_r16<Bf16, 256, 32, false, 2, true>, nullptr},
-    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1, false>, attn_fwd16_r16<Bf16, 512, 32, true, 1, true>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2, false>, attn_fwd16<F16, 32, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2, false>, attn_fwd16<F16, 64, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2, false>, attn_fwd16<F16, 128, 64, 4, 2, true>, nullptr},
-    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1, false>, attn_fwd16_r16<F16, 256, 64, false, 1, true>, nullptr},
-    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2, false>, attn_fwd16_r16<F16, 256, 32, false, 2, true>, nullptr},
-    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1, false>, attn_fwd16_r16<F16, 512, 32, true, 1, true>, pack_v_operands<512, 32, true>},
-    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<32, 32>, attn_fwd32<32, 32>, nullptr},
-    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<64, 32>, attn_fwd32<64, 32>, nullptr},
-    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<128, 32>, attn_fwd32<128, 32>, nullptr},
-    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, attn_fwd32<256, 32>, nullptr},
+    {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 32, 64, 4, 2, kRing>, attn_fwd16<Bf16, 32, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 64, 64, 4, 2, kRing>, attn_fwd16<Bf16, 64, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 128, 64, 4, 2, kRing>, attn_fwd16<Bf16, 128, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1, kLinear>, attn_fwd16_r16<Bf16, 256, 64, false, 1, kRing>, attn_fwd16_r16<Bf16, 256, 64, false, 1, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2, kLinear>, attn_fwd16_r16<Bf16, 256, 32, false, 2, kRing>, attn_fwd16_r16<Bf16, 256, 32, false, 2, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1, kLinear>, attn_fwd16_r16<Bf16, 512, 32, true, 1, kRing>, attn_fwd16_r16<Bf16, 512, 32, true, 1, kPaged>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 0, attn_fwd16_r16<Bf16, 512, 32, false, 1, kLinear>, attn_fwd16_r16<Bf16, 512, 32, false, 1, kRing>, attn_fwd16_r16<Bf16, 512, 32, false, 1, kPaged>, nullptr},
+    {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2, kLinear>, attn_fwd16<F16, 32, 64, 4, 2, kRing>, attn_fwd16<F16, 32, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2, kLinear>, attn_fwd16<F16, 64, 64, 4, 2, kRing>, attn_fwd16<F16, 64, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2, kLinear>, attn_fwd16<F16, 128, 64, 4, 2, kRing>, attn_fwd16<F16, 128, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1, kLinear>, attn_fwd16_r16<F16, 256, 64, false, 1, kRing>, attn_fwd16_r16<F16, 256, 64, false, 1, kPaged>, nullptr},
+    {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2, kLinear>, attn_fwd16_r16<F16, 256, 32, false, 2, kRing>, attn_fwd16_r16<F16, 256, 32, false, 2, kPaged>, nullptr},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1, kLinear>, attn_fwd16_r16<F16, 512, 32, true, 1, kRing>, attn_fwd16_r16<F16, 512, 32, true, 1, kPaged>, pack_v_operands<512, 32, true>},
+    {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 0, attn_fwd16_r16<F16, 512, 32, false, 1, kLinear>, attn_fwd16_r16<F16, 512, 32, false, 1, kRing>, attn_fwd16_r16<F16, 512, 32, false, 1, kPaged>, nullptr},
+    {PA_DTYPE_F32, 32, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<32, 32>, attn_fwd32<32, 32>, attn_fwd32<32, 32>, nullptr},
+    {PA_DTYPE_F32, 64, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<64, 32>, attn_fwd32<64, 32>, attn_fwd32<64, 32>, nullptr},
+    {PA_DTYPE_F32, 128, 32, 2, kThreads, kRowsPerGroup, 1, attn_fwd32<128, 32>, attn_fwd32<128, 32>, attn_fwd32<128, 32>, nullptr},
+    {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, attn_fwd32<256, 32>, attn_fwd32<256, 32>, nullptr},
 };
 
 using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
+using WideMergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int);
+
+// splits above which the merge reads them in parallel (merge_splits_wide)
+constexpr int kWideMergeSplits = 8;
+
+WideMergeFn wide_merge_for(int D) {
+    switch (D) {
+        case 32: return merge_splits_wide<32>;
+        case 64: return merge_splits_wide<64>;
+        case 128: return merge_splits_wide<128>;
+        case 256: return merge_splits_wide<256>;
+        case 512: return merge_splits_wide<512>;
+    }
+    return nullptr;
+}
 
 MergeFn merge_for(int D) {
     switch (D) {
@@ -1368,10 +1522,11 @@ const Variant *find_variant(int dtype, int D) {
 }
 
 // The variant whose work-groups split each tile's keys between two halves of
-// their wavefronts, if this dtype and head_dim have one.
-const Variant *find_ksplit_variant(int dtype, int D) {
+// their wavefronts (ksplit 2), or the one that reads V in place instead of an
+// operand-order copy (ksplit 0), if this dtype and head_dim have one.
+const Variant *find_ksplit_variant(int dtype, int D, int ksplit = 2) {
     for (const Variant &v : kVariants)
-        if (v.dtype == dtype && v.D == D && v.ksplit == 2) return &v;
+        if (v.dtype == dtype && v.D == D && v.ksplit == ksplit) return &v;
     return nullptr;
 }
 
@@ -1387,6 +1542,9 @@ struct Plan {
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kMaxSplits = 256;
+constexpr int kMinQueryTilesForPack = 8;
 
 int first_key_host(int64_t pos, int window) {
     return (window > 0 && pos - window + 1 > 0) ? (int)(pos - window + 1) : 0;
@@ -1409,6 +1567,10 @@ int check_shape(int dtype, int T, int start_pos, int H, int KVH, int D, int wind
 // cost of writing and merging its partial rows.
 int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int window,
                   int G, int TQ, int nq) {
+    // a split's partial rows (written, then merged) cost about half a KV tile's
+    // work when the query tile is full, proportionally less for short chunks
+    const int rows = std::min(T, TQ) * G;
+    const double split_cost = 0.5 * std::min(1.0, (double)rows / var.rows);
     const int slots = kCus * var.groups_per_cu;
     const int64_t base = (int64_t)nq * KVH;
     if (base >= slots) return 1;
@@ -1421,13 +1583,13 @@ int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int 
     }
     int best = 1;
     double best_cost = 1e300;
-    for (int S = 1; S <= 16; ++S) {
+    for (int S = 1; S <= kMaxSplits; ++S) {
         if (S > 1 && cdiv(max_tiles, S) < 4) break;
         const int64_t items = base * S;
         const double waves = (double)cdiv(items, slots);
         // one tile's time is the unit; a split adds a partial-row write+merge
         // of roughly half a tile for its work-group
-        const double cost = waves * (double)cdiv(max_tiles, S) + (S > 1 ? 0.5 * S : 0.0);
+        const double cost = waves * (double)cdiv(max_tiles, S) + (S > 1 ? split_cost * S : 0.0);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best = S;
@@ -1449,6 +1611,11 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
         const int64_t base = cdiv(T, var->rows / (H / KVH)) * KVH;
         if (base < (int64_t)kCus * var->groups_per_cu && alt->rows >= H / KVH) var = alt;
     }
+    // The V operand-order copy costs a pass over the call's V rows and pays
+    // off through their reuse by many query tiles; short chunks (decode,
+    // draft verification) read V in place.
+    if (var->pack && cdiv(T, var->rows / (H / KVH)) < kMinQueryTilesForPack)
+        if (const Variant *alt = find_ksplit_variant(dtype, D, 0)) var = alt;
     pl->var = var;
     pl->G = H / KVH;
     pl->TQ = var->rows / pl->G;
@@ -1489,11 +1656,19 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-// ring: slots per kv head of a ring cache (key j in slot j % ring), 0 for a
-// linear cache (key j in row j).
+// Where key j of a kv head lives: row j (linear), slot j % ring (ring > 0),
+// or page page_table[j >> page_shift] of a pool of num_pages pages (paged).
+struct CacheLayout {
+    int ring = 0;
+    const int32_t *page_table = nullptr;
+    int page_shift = 0, num_pages = 0;
+};
+
 int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const void *k,
-           const void *v, int64_t kv_head_stride, int ring, float *out, int64_t out_row_stride,
-           int T, int start_pos, int H, int KVH, int D, int window, void *ws, hipStream_t stream) {
+           const void *v, int64_t kv_head_stride, const CacheLayout &lay, float *out,
+           int64_t out_row_stride, int T, int start_pos, int H, int KVH, int D, int window, void *ws,
+           hipStream_t stream) {
+    const int ring = lay.ring;
     Params p;
     p.q = q;
     p.k = k;
@@ -1521,18 +1696,25 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.order = pl.var->groups_per_cu == 2 ? 1 : 0;
     p.L = start_pos + T;
     p.ring = ring;
+    p.page_table = lay.page_table;
+    p.page_shift = lay.page_shift;
+    p.num_pages = lay.num_pages;
     p.kv_bytes = (int)std::min<int64_t>((ring ? (int64_t)ring : (int64_t)start_pos + T) * D *
                                             elem_bytes(dtype), INT32_MAX);
     if (pl.var->pack) {
-        hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream,
-                           (const uint16_t *)v, kv_head_stride, start_pos + T, ring, pl.vop_kt_lo,
-                           pl.vop_tiles, (uint16_t *)ws);
+        hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream, p,
+                           (uint16_t *)ws);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     }
-    hipLaunchKernelGGL(ring ? pl.var->fn_ring : pl.var->fn, dim3(pl.items), dim3(pl.var->threads), 0,
-                       stream, p);
+    const KernelFn fn = lay.page_table ? pl.var->fn_paged : ring ? pl.var->fn_ring : pl.var->fn;
+    hipLaunchKernelGGL(fn, dim3(pl.items), dim3(pl.var->threads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-    if (pl.S > 1) {
+    if (pl.S > kWideMergeSplits) {
+        hipLaunchKernelGGL(wide_merge_for(D), dim3((unsigned)((int64_t)T * H)), dim3(512), 0, stream,
+                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_row_stride, T, H,
+                           pl.S);
+        if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    } else if (pl.S > 1) {
         const int64_t n = (int64_t)T * H * (D / 4);
         hipLaunchKernelGGL(merge_for(D), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
                            (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_row_stride, T, H,
@@ -1610,14 +1792,14 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
     void *ws = nullptr;
     st = scratch_for(pl.ws_bytes, &ws);
     if (st != PA_OK) return st;
-    return launch(pl, dtype, q, row, k, v, kvs, 0, out, row, T, start_pos, H, KVH, D, window, ws,
-                  (hipStream_t)stream);
+    return launch(pl, dtype, q, row, k, v, kvs, CacheLayout{}, out, row, T, start_pos, H, KVH, D,
+                  window, ws, (hipStream_t)stream);
 }
 
 // Plan, workspace check and launch of the strided entry points (arguments checked).
 int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
-           int64_t kv_head_stride, int ring, float *out, int64_t out_row_stride, int T,
-           int start_pos, int H, int KVH, int D, int window, void *workspace,
+           int64_t kv_head_stride, const CacheLayout &lay, float *out, int64_t out_row_stride,
+           int T, int start_pos, int H, int KVH, int D, int window, void *workspace,
            size_t workspace_bytes, void *stream) {
     Plan pl;
     const int st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
@@ -1626,7 +1808,7 @@ int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const 
         if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
     }
-    return launch(pl, dtype, q, q_row_stride, k, v, kv_head_stride, ring, out, out_row_stride, T,
+    return launch(pl, dtype, q, q_row_stride, k, v, kv_head_stride, lay, out, out_row_stride, T,
                   start_pos, H, KVH, D, window, workspace, (hipStream_t)stream);
 }
 
@@ -1666,8 +1848,8 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *
                         (int64_t)start_pos + T, out, out_row_stride, T, start_pos, num_heads,
                         num_kv_heads, head_dim, window);
     if (st != PA_OK) return st;
-    return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, 0, out, out_row_stride,
-                  T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+    return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
+                  out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
 }
 
@@ -1686,9 +1868,33 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const v
     const int64_t need = window > 0 ? std::min<int64_t>(L, (int64_t)window + T - 1) : L;
     if (ring_slots < need) return PA_ERR_INVALID_ARG;
     // a ring at least as long as the call is a linear cache (slot j holds key j)
-    return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride,
-                  ring_slots >= L ? 0 : ring_slots, out, out_row_stride, T, start_pos, num_heads,
-                  num_kv_heads, head_dim, window, workspace, workspace_bytes, stream);
+    CacheLayout lay;
+    lay.ring = ring_slots >= L ? 0 : (int)ring_slots;
+    return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride, lay, out, out_row_stride,
+                  T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+                  workspace_bytes, stream);
+}
+
+int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_pool,
+                          const void *v_pool, int page_size, int num_pages,
+                          const int32_t *page_table, float *out, int64_t out_row_stride, int T,
+                          int start_pos, int num_heads, int num_kv_heads, int head_dim, int window,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (!page_table || num_pages < 1) return PA_ERR_INVALID_ARG;
+    // a page holds whole KV tiles of every kernel (64 keys at most)
+    if (page_size < 64 || (page_size & (page_size - 1)) != 0) return PA_ERR_UNSUPPORTED;
+    // the pool's pages as the head stride of a linear cache of num_pages*page_size
+    // rows: the shape and pointer checks are those of prefill_attn_ex
+    int st = check_args(dtype, q, q_row_stride, k_pool, v_pool, (int64_t)page_size * head_dim,
+                        page_size, out, out_row_stride, T, start_pos, num_heads, num_kv_heads,
+                        head_dim, window);
+    if (st != PA_OK) return st;
+    CacheLayout lay;
+    lay.page_table = page_table;
+    lay.page_shift = __builtin_ctz((unsigned)page_size);
+    lay.num_pages = num_pages;
+    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, T, start_pos,
+                  num_heads, num_kv_heads, head_dim, window, workspace, workspace_bytes, stream);
 }
 
 int prefill_kv_write(int dtype, const void *k_src, const void *v_src, int64_t src_row_stride,

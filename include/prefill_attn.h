@@ -136,6 +136,28 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride,
                          int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Paged cache form (short chunks and decode over a shared pool; the FreeToken
+ * page "perf(spec): capture the gemma4 assistant draft in cuda graphs": each
+ * draft step reads the sequence's [0, cached_len) keys through its page
+ * table).  k_pool and v_pool hold num_pages pages; page pg holds page_size
+ * consecutive positions of every kv head:
+ *     k_pool[((pg*num_kv_heads + kh)*page_size + r)*head_dim + d]   (v_pool alike)
+ * and key j of kv head kh is row j % page_size of page page_table[j / page_size].
+ * page_table is device memory (int32) with at least ceil(L / page_size)
+ * entries; it is read by the kernels, so it may be rewritten between calls
+ * (e.g. inside a captured graph's fixed buffer).  page_size must be a power
+ * of two >= 64 (every KV tile then lies in one page).  Entries of blocks that
+ * no row reads (below every row's window) may hold anything; an entry outside
+ * [0, num_pages) reads as zeros (no fault).  Everything else is
+ * prefill_attn_ex, including the workspace it needs for the same shape.
+ */
+int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride,
+                          const void *k_pool, const void *v_pool, int page_size, int num_pages,
+                          const int32_t *page_table, float *out, int64_t out_row_stride,
+                          int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                          int window, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * KV cache write, the step before the attention (gnosis page, "What already
  * shipped": Phase A stores each token's K/V in the cache; TensorSharp page,
  * section 4, requirement R4: global layers append at row start_pos + i,

@@ -19,7 +19,8 @@ def test_exports_every_declared_function(lib):
     names = pa.header_functions()
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
                           "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
-                          "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write"}
+                          "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write",
+                          "prefill_attn_paged_ex"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,3 +166,23 @@ def test_kv_write_arguments(lib):
     assert call(d=4) == U                      # 8-byte rows
     assert call(ks=FAKE + 8) == U              # misaligned
     assert call(srs=KVH * D + 4) == U          # source rows not 16-byte multiples
+
+
+def test_paged_arguments(lib):
+    """prefill_attn_paged_ex refuses bad page sizes, a missing table or pool
+    size, and every bad shape prefill_attn_ex refuses, before enqueuing."""
+    px = lib.prefill_attn_paged_ex
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    H, KVH, D = 8, 2, 128
+
+    def call(P=256, npages=10, table=FAKE, T=4, sp=1000, w=0, dtype=1, q=FAKE):
+        return px(dtype, q, H * D, FAKE, FAKE, P, npages, table, FAKE, H * D, T, sp, H, KVH, D, w,
+                  None, 0, None)
+
+    assert call(table=None) == E
+    assert call(npages=0) == E
+    assert call(P=32) == U and call(P=96) == U and call(P=0) == U
+    assert call(T=0) == E and call(sp=-1) == E and call(w=-2) == E
+    assert call(q=None) == E
+    assert call(dtype=5) == U
+    assert call(q=FAKE + 2) == U

@@ -199,7 +199,7 @@ def _run_workload(orc, name, n_random=64):
     wl = workloads.WORKLOADS[name]
     x = workloads.make_inputs(wl)
     H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
-    if not wl.ring:
+    if not wl.ring and not wl.page_size:
         k = to_device(x.k_store, wl.dtype)
         v = to_device(x.v_store, wl.dtype)
     for ci, (T, sp) in enumerate(wl.chunks):
@@ -208,7 +208,16 @@ def _run_workload(orc, name, n_random=64):
         out = torch.empty(T, H * D, device=device())
         ws_b = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
         ws = torch.empty(ws_b, dtype=torch.uint8, device=device()) if ws_b else None
-        if wl.ring:
+        if wl.page_size:
+            L = sp + T
+            npages = -(-L // wl.page_size) + 16
+            nan = np.uint16(0x7FC0) if wl.dtype == "bf16" else np.uint16(0x7E00)
+            kp, table = workloads.paged_cache(x.k_store, wl.page_size, L, npages, wl.seed, nan)
+            vp, _ = workloads.paged_cache(x.v_store, wl.page_size, L, npages, wl.seed, nan)
+            pa.prefill_attn_paged_ex(q, H * D, to_device(kp, wl.dtype), to_device(vp, wl.dtype),
+                                     wl.page_size, torch.from_numpy(table).to(device()), out, H * D,
+                                     T, sp, H, KVH, D, W, workspace=ws)
+        elif wl.ring:
             # the ring as the cache writes up to this chunk's last key leave it
             nan = np.uint16(0x7FC0) if wl.dtype == "bf16" else np.uint16(0x7E00)
             k = to_device(workloads.ring_cache(x.k_store, wl.ring, sp + T, nan), wl.dtype)
@@ -255,3 +264,7 @@ def test_workload_gemma_swa_bf16(orc):
 
 def test_workload_gemma_swa_bf16_ring(orc):
     _run_workload(orc, "gemma_swa_bf16_ring")
+
+
+def test_workload_gemma_global_verify_paged(orc):
+    _run_workload(orc, "gemma_global_verify_paged")

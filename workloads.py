@@ -41,6 +41,7 @@ class Workload:
     seed: int
     summary: str = ""
     ring: int = 0                    # > 0: the GPU reads K/V from a ring of this many slots
+    page_size: int = 0               # > 0: the GPU reads K/V from a paged pool of this page size
 
     @property
     def q_tokens(self) -> int:
@@ -80,6 +81,12 @@ WORKLOADS = {
         "gemma_swa_bf16_ring", "bf16", 8, 4, 256, 1024, ((2048, 129024),), 131072, 0.3, 105,
         "Gemma-style sliding-window layer as gemma_swa_bf16, K/V in a ring cache of 3072 slots "
         "(key j in slot j % 3072)", ring=3072),
+    # a verify step of three drafted tokens (T = 4) over the global layer's
+    # 61440 cached keys, read through a page table of 256-position pages
+    "gemma_global_verify_paged": Workload(
+        "gemma_global_verify_paged", "bf16", 8, 2, 512, 0, ((4, 61440),), 61444, 0.3, 106,
+        "Gemma-style global layer, 8/2 heads, head_dim 512: a T=4 verify step at start_pos 61440 "
+        "over a paged cache of 256-position pages", page_size=256),
 }
 
 
