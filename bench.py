@@ -37,7 +37,6 @@ METRIC = "prefill attention TFLOP/s and % of MI355X bf16 MFMA peak (T=2048 chunk
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_GBS = 8000.0
 WARMUP_S = 0.3
-RIDGE_FLOP_PER_BYTE = 2516.6e12 / 8e12   # bf16 MFMA peak over HBM bandwidth
 KERNEL_SOURCE = os.path.join(ROOT, "causal_gqa_attention_prefill_amd", "csrc", "prefill_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -379,8 +378,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
     }
-    if flops_step / bytes_step < RIDGE_FLOP_PER_BYTE:
-        # below the ridge (short chunks over long caches): priced against HBM
+    if flops_step / bytes_step < peak * 1e12 / (HBM_GBS * 1e9):
+        # below the ridge of the dtype's matrix peak over HBM bandwidth (short
+        # chunks over long caches): priced against HBM
         gbs = bytes_step / len(calls) / (mean_launch_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS,
                               "unit": "GB/s", "frac": round(gbs / HBM_GBS, 4), "traffic": traffic}
