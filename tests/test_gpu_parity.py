@@ -46,6 +46,17 @@ def test_small_full(orc, dtype, D, H, KVH, T, sp, W):
     assert_parity(got, ref, dtype, f"{dtype} D{D} {H}/{KVH} T{T} sp{sp} W{W}")
 
 
+@pytest.mark.parametrize("dtype,D,H,KVH,T,sp,W", [("bf16", 64, 128, 1, 5, 40, 0), ("f16", 128, 96, 1, 3, 300, 0),
+                                                  ("bf16", 256, 128, 1, 2, 100, 30), ("bf16", 512, 128, 2, 3, 77, 0),
+                                                  ("f32", 32, 128, 1, 4, 9, 0)])
+def test_largest_groups(orc, dtype, D, H, KVH, T, sp, W):
+    """Query-head groups up to the work-group's 128 rows (one token per tile)."""
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=H + D + T, dtype=dtype)
+    got = run_packed(x, T, sp, H, KVH, D, W)
+    ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W)
+    assert_parity(got, ref, dtype, f"group {H // KVH} {dtype} D{D}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_peaked_softmax(orc, dtype):
     """Q scaled up 16x: peaked rows, large running-max jumps and rescales."""
