@@ -59,6 +59,9 @@ def load():
     lib.prefill_attn_paged_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, I, I, I, I, I, P, SZ,
                                           P]
     lib.prefill_attn_paged_ex.restype = I
+    lib.prefill_attn_paged_dev_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, P, I, I, I, I, I,
+                                              P, SZ, P]
+    lib.prefill_attn_paged_dev_ex.restype = I
     lib.prefill_kv_write.restype = I
     lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.prefill_attn_workspace_bytes.restype = SZ
@@ -160,7 +163,8 @@ class PreparedCall:
 
     def __init__(self, q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                  start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
-                 stream=None, ring_slots=None, page_table=None, page_size=None):
+                 stream=None, ring_slots=None, page_table=None, page_size=None,
+                 start_pos_dev=None):
         dt = _dtype_of(q)
         if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
             raise TypeError("q, k_cache and v_cache must share one storage type")
@@ -186,7 +190,20 @@ class PreparedCall:
                 v_cache.data_ptr(), kv_head_stride)
         tail = (out.data_ptr(), out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim,
                 window, ws_ptr, ws_bytes, _stream(stream))
-        if page_table is not None:
+        if start_pos_dev is not None:
+            # start_pos is the largest the device value may take
+            import torch
+            if page_table is None or start_pos_dev.dtype != torch.int32:
+                raise TypeError("start_pos_dev needs a paged cache and an int32 device tensor")
+            _need(start_pos_dev, 1, "start_pos_dev")
+            self._name, self._fn = "prefill_attn_paged_dev_ex", load().prefill_attn_paged_dev_ex
+            self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                          v_cache.data_ptr(), int(page_size),
+                          k_cache.numel() // (page_size * num_kv_heads * head_dim),
+                          page_table.data_ptr(), out.data_ptr(), out_row_stride, T,
+                          start_pos_dev.data_ptr(), start_pos, num_heads, num_kv_heads, head_dim,
+                          window, ws_ptr, ws_bytes, _stream(stream))
+        elif page_table is not None:
             self._name, self._fn = "prefill_attn_paged_ex", load().prefill_attn_paged_ex
             self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
                           v_cache.data_ptr(), int(page_size),
@@ -197,7 +214,7 @@ class PreparedCall:
         else:
             self._name, self._fn = "prefill_attn_ring_ex", load().prefill_attn_ring_ex
             self._args = head + (int(ring_slots),) + tail
-        self._keep = (q, k_cache, v_cache, out, workspace, page_table)
+        self._keep = (q, k_cache, v_cache, out, workspace, page_table, start_pos_dev)
         self.out = out
 
     def __call__(self):

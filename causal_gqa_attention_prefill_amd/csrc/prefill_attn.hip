@@ -93,10 +93,21 @@ struct Params {
     int ring;         // ring cache: key j sits in slot j % ring of its kv head; 0: row j
     const int32_t *page_table;  // paged cache: page of each block of 2^page_shift keys (else null)
     int page_shift, num_pages;
+    const int32_t *start_pos_dev;  // device-side start_pos (at most start_pos), else null
     const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
     int vop_kt_lo;         // first KV tile held in vop
     int vop_tiles;         // KV tiles per kv head held in vop
 };
+
+// A call whose start_pos sits in device memory (so that one captured graph
+// serves every length): the plan was made for the largest start_pos, passed
+// in p.start_pos; the work-groups take the current one.
+__device__ inline void take_device_start(Params &p) {
+    if (p.start_pos_dev) {
+        p.start_pos = min(max(*p.start_pos_dev, 0), p.start_pos);
+        p.L = p.start_pos + p.T;
+    }
+}
 
 // K/V cache layouts: key j of kv head kh is row j of the head's block
 // (linear), slot j % ring of it (ring, sliding-window layers), or row
@@ -535,6 +546,7 @@ template <class Ty, int D, int BK, int NW, int WAVES_PER_SIMD, int LAYOUT>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD)))
 void attn_fwd16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    take_device_start(p);
     static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
     constexpr int CPR = D / 8;                        // 16-byte chunks per row
     constexpr int ROW_BYTES = CPR * 16;
@@ -822,6 +834,7 @@ template <class Ty, int D, int BK, bool VPACK, int KSPLIT, int LAYOUT>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    take_device_start(p);
     static_assert(D >= 128 && D % 32 == 0 && BK % 32 == 0, "tile shape");
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && !VPACK), "key halves read V in place");
     constexpr int NWH = kWaves16 / KSPLIT;            // wavefronts per key half
@@ -1172,6 +1185,7 @@ __device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
 template <int D, int BK>
 __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
     static_assert(D % 32 == 0 && BK % 32 == 0, "tile shape");
+    take_device_start(p);
     constexpr int KROW = D + 4;           // floats; 16 B of padding
     constexpr int VROW = BK + 4;
     constexpr int KVEC = BK * D / 4;
@@ -1600,7 +1614,8 @@ int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int 
     return best;
 }
 
-int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window, Plan *pl) {
+int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window, Plan *pl,
+              bool no_pack = false) {
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st != PA_OK) return st;
     const Variant *var = find_variant(dtype, D);
@@ -1614,7 +1629,9 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     // The V operand-order copy costs a pass over the call's V rows and pays
     // off through their reuse by many query tiles; short chunks (decode,
     // draft verification) read V in place.
-    if (var->pack && cdiv(T, var->rows / (H / KVH)) < kMinQueryTilesForPack)
+    // (a start_pos known only on the device also reads V in place: the copy
+    // covers the call's tiles, which the host plan cannot know)
+    if (var->pack && (no_pack || cdiv(T, var->rows / (H / KVH)) < kMinQueryTilesForPack))
         if (const Variant *alt = find_ksplit_variant(dtype, D, 0)) var = alt;
     pl->var = var;
     pl->G = H / KVH;
@@ -1662,6 +1679,7 @@ struct CacheLayout {
     int ring = 0;
     const int32_t *page_table = nullptr;
     int page_shift = 0, num_pages = 0;
+    const int32_t *start_pos_dev = nullptr;   // start_pos read by the kernels (planned for the max)
 };
 
 int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const void *k,
@@ -1699,6 +1717,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.page_table = lay.page_table;
     p.page_shift = lay.page_shift;
     p.num_pages = lay.num_pages;
+    p.start_pos_dev = lay.start_pos_dev;
     p.kv_bytes = (int)std::min<int64_t>((ring ? (int64_t)ring : (int64_t)start_pos + T) * D *
                                             elem_bytes(dtype), INT32_MAX);
     if (pl.var->pack) {
@@ -1802,7 +1821,7 @@ int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const 
            int T, int start_pos, int H, int KVH, int D, int window, void *workspace,
            size_t workspace_bytes, void *stream) {
     Plan pl;
-    const int st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
+    const int st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl, lay.start_pos_dev != nullptr);
     if (st != PA_OK) return st;
     if (pl.ws_bytes > 0) {
         if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
@@ -1872,6 +1891,29 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const v
     lay.ring = ring_slots >= L ? 0 : (int)ring_slots;
     return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride, lay, out, out_row_stride,
                   T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+                  workspace_bytes, stream);
+}
+
+int prefill_attn_paged_dev_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_pool,
+                              const void *v_pool, int page_size, int num_pages,
+                              const int32_t *page_table, float *out, int64_t out_row_stride, int T,
+                              const int32_t *start_pos_dev, int max_start_pos, int num_heads,
+                              int num_kv_heads, int head_dim, int window, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (!start_pos_dev) return PA_ERR_INVALID_ARG;
+    if (!page_table || num_pages < 1) return PA_ERR_INVALID_ARG;
+    if (page_size < 64 || (page_size & (page_size - 1)) != 0) return PA_ERR_UNSUPPORTED;
+    int st = check_args(dtype, q, q_row_stride, k_pool, v_pool, (int64_t)page_size * head_dim,
+                        page_size, out, out_row_stride, T, max_start_pos, num_heads, num_kv_heads,
+                        head_dim, window);
+    if (st != PA_OK) return st;
+    CacheLayout lay;
+    lay.page_table = page_table;
+    lay.page_shift = __builtin_ctz((unsigned)page_size);
+    lay.num_pages = num_pages;
+    lay.start_pos_dev = start_pos_dev;
+    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, T,
+                  max_start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
 }
 

@@ -158,6 +158,23 @@ int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride,
                           int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The paged form with start_pos in device memory: *start_pos_dev (int32,
+ * read by the kernels when they run) replaces start_pos, so one captured
+ * graph serves every length of a decode or draft loop (the FreeToken page
+ * copies the cached length into a fixed buffer before each replay).  The
+ * launch is planned for max_start_pos, which bounds the device value (larger
+ * values are clamped to it, negative ones to 0); the workspace is the one
+ * prefill_attn_workspace_bytes gives for max_start_pos.  The page table must
+ * cover max_start_pos + T keys.
+ */
+int prefill_attn_paged_dev_ex(int dtype, const void *q, int64_t q_row_stride,
+                              const void *k_pool, const void *v_pool, int page_size, int num_pages,
+                              const int32_t *page_table, float *out, int64_t out_row_stride,
+                              int T, const int32_t *start_pos_dev, int max_start_pos,
+                              int num_heads, int num_kv_heads, int head_dim, int window,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * KV cache write, the step before the attention (gnosis page, "What already
  * shipped": Phase A stores each token's K/V in the cache; TensorSharp page,
  * section 4, requirement R4: global layers append at row start_pos + i,

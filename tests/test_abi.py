@@ -20,7 +20,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
                           "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
                           "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write",
-                          "prefill_attn_paged_ex"}
+                          "prefill_attn_paged_ex", "prefill_attn_paged_dev_ex"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -186,3 +186,21 @@ def test_paged_arguments(lib):
     assert call(q=None) == E
     assert call(dtype=5) == U
     assert call(q=FAKE + 2) == U
+
+
+def test_paged_dev_arguments(lib):
+    """The device-start form needs its start buffer and checks the rest as the
+    paged form does, for the largest start_pos."""
+    px = lib.prefill_attn_paged_dev_ex
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    H, KVH, D = 8, 2, 128
+
+    def call(sp_dev=FAKE, maxsp=1000, P=256, table=FAKE, T=4):
+        return px(1, FAKE, H * D, FAKE, FAKE, P, 10, table, FAKE, H * D, T, sp_dev, maxsp, H, KVH, D, 0,
+                  None, 0, None)
+
+    assert call(sp_dev=None) == E
+    assert call(table=None) == E
+    assert call(maxsp=-1) == E
+    assert call(T=0) == E
+    assert call(P=48) == U

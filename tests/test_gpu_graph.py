@@ -65,3 +65,65 @@ def test_graph_replay_of_chunk_loop(orc):
         with torch.cuda.stream(side):   # eager work between replays
             loop()
         torch.cuda.synchronize()
+
+
+def test_graph_replay_over_lengths(orc):
+    """One captured graph of a verify step (T = 4) over a paged cache, its start
+    position in a device buffer that is rewritten before each replay together
+    with the query rows and the cache contents (as the FreeToken page copies
+    the cached length and pending tokens into fixed buffers): every replay, at
+    lengths from 100 to 8000 keys, matches the oracle and the same call made
+    with a host start_pos, bit for bit."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    pa.load()
+    H, KVH, D, T, P = 16, 4, 128, 4, 256
+    max_sp = 7996
+    N = max_sp + T
+    npages = -(-N // P) + 5
+    x = workloads.make_random(H, KVH, D, N, 0, std=0.5, seed=51, dtype="bf16")
+    nan = np.uint16(0x7FC0)
+    _, table_full = workloads.paged_cache(x.k_store, P, N, npages, seed=9, fill=nan)
+    side = torch.cuda.Stream()
+    q_buf = torch.empty(T, H * D, dtype=torch.bfloat16, device=device())
+    kpool = torch.empty(npages * KVH * P * D, dtype=torch.bfloat16, device=device())
+    vpool = torch.empty_like(kpool)
+    table = torch.from_numpy(table_full).to(device())
+    sp_buf = torch.zeros(1, dtype=torch.int32, device=device())
+    out = torch.empty(T, H * D, device=device())
+    out_host = torch.empty_like(out)
+    nb = pa.workspace_bytes("bf16", T, max_sp, H, KVH, D, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=device())
+    dev_call = pa.PreparedCall(q_buf, H * D, kpool, vpool, 0, out, H * D, T, max_sp, H, KVH, D, 0,
+                               workspace=ws, stream=side, page_table=table, page_size=P,
+                               start_pos_dev=sp_buf)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dev_call()
+    torch.cuda.synchronize()
+    for sp in (100, 1234, 4000, max_sp):
+        L = sp + T
+        kp, _ = workloads.paged_cache(x.k_store[:, :L], P, L, npages, seed=9, fill=nan)
+        vp, _ = workloads.paged_cache(x.v_store[:, :L], P, L, npages, seed=9, fill=nan)
+        kpool.copy_(to_device(kp, "bf16").reshape(-1))
+        vpool.copy_(to_device(vp, "bf16").reshape(-1))
+        q_buf.copy_(to_device(x.q_store[sp:sp + T], "bf16"))
+        sp_buf.fill_(sp)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            g.replay()
+        torch.cuda.synchronize()
+        ref = orc.attention(x.q_f32[sp:sp + T], x.k_f32[:, :L], x.v_f32[:, :L], T, sp, H, KVH, D,
+                            kv_head_stride=L * D)
+        got = out.cpu().numpy().reshape(T, H, D)
+        assert_parity(got, ref, "bf16", f"replay at start_pos {sp}")
+        nbh = pa.workspace_bytes("bf16", T, sp, H, KVH, D, 0)
+        wsh = torch.empty(nbh, dtype=torch.uint8, device=device()) if nbh else None
+        pa.prefill_attn_paged_ex(q_buf, H * D, kpool, vpool, P, table, out_host, H * D, T, sp, H,
+                                 KVH, D, 0, workspace=wsh)
+        torch.cuda.synchronize()
+        if pa.plan("bf16", T, sp, H, KVH, D, 0)["kv_splits"] == pa.plan("bf16", T, max_sp, H, KVH, D, 0)["kv_splits"]:
+            assert torch.equal(out, out_host), sp
+        else:
+            assert_parity(out_host.cpu().numpy().reshape(T, H, D), ref, "bf16", f"host start {sp}")
