@@ -311,6 +311,7 @@ __device__ inline float softmax_max(const f32x16 (&s)[NB], float &m, float c, fl
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+#define LDS_ADDR(a) ((__attribute__((address_space(3))) void *)(uintptr_t)(a))
 #define LDS_I16X4(p) ((__attribute__((address_space(3))) i16x4 *)(p))
 
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer descriptors exist in the device pass only
@@ -626,14 +627,19 @@ void attn_fwd16(Params p) {
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
     auto issue = [&](int kt, int kdst, int vdst) {
+        // LDS destination (M0) of this wave's chunks: one scalar base, made
+        // opaque at every issue so that the compiler derives the per-chunk
+        // values here instead of keeping all sixteen live through the loop
+        uint32_t mb = (uint32_t)(uintptr_t)LDS_PTR(smem) + wave * LOADS * 1024;
+        asm volatile("" : "+s"(mb));
         if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+                    rk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], base, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], base, 0, 0);
+                    rv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], base, 0, 0);
             }
         } else if constexpr (LAYOUT == kPaged) {
             __amdgpu_buffer_rsrc_t pk, pv;
@@ -642,9 +648,9 @@ void attn_fwd16(Params p) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, koff[i], soff, 0, 0);
+                    pk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], soff, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, voff[i], soff, 0, 0);
+                    pv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], soff, 0, 0);
             }
             pg_next = page_of(p, (kt + 1) * BK);     // one tile ahead of its use
         } else {
@@ -654,9 +660,9 @@ void attn_fwd16(Params p) {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_PTR(smem + kdst + (wave * LOADS + i) * 1024), 16, ko[i], ks, 0, 0);
+                    rk, LDS_ADDR(mb + kdst + i * 1024), 16, ko[i], ks, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_PTR(smem + vdst + (wave * LOADS + i) * 1024), 16, vo[i], vs, 0, 0);
+                    rv, LDS_ADDR(mb + vdst + i * 1024), 16, vo[i], vs, 0, 0);
             }
         }
     };
