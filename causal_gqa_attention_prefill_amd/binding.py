@@ -51,16 +51,17 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [P, P, P, P] + tail
         fn.restype = I
-    lib.prefill_attn_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, P, SZ, P]
+    lib.prefill_attn_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, I, P, SZ, P]
     lib.prefill_attn_ex.restype = I
-    lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, P, SZ, P]
+    lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, I, P, SZ,
+                                         P]
     lib.prefill_attn_ring_ex.restype = I
     lib.prefill_kv_write.argtypes = [I, P, P, I64, P, P, I64, I, I, I, I, I, P]
-    lib.prefill_attn_paged_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, I, I, I, I, I, P, SZ,
-                                          P]
+    lib.prefill_attn_paged_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, I, I, I, I, I, I, P,
+                                          SZ, P]
     lib.prefill_attn_paged_ex.restype = I
-    lib.prefill_attn_paged_dev_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, P, I, I, I, I, I,
-                                              P, SZ, P]
+    lib.prefill_attn_paged_dev_ex.argtypes = [I, P, I64, P, P, I, I, P, P, I64, I, I, P, I, I, I, I,
+                                              I, P, SZ, P]
     lib.prefill_attn_paged_dev_ex.restype = I
     lib.prefill_kv_write.restype = I
     lib.prefill_attn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -154,7 +155,8 @@ def prefill_attn(q, k_cache, v_cache, out, T, start_pos, num_heads, num_kv_heads
 
 class PreparedCall:
     """prefill_attn_ex (prefill_attn_ring_ex when ring_slots is given) with
-    its arguments checked and marshalled once.
+    its arguments checked and marshalled once.  out may be float32, bfloat16
+    or float16 (out_dtype follows its dtype).
 
     For callers that launch the same call repeatedly (a chunk loop, a
     benchmark): calling the object issues just the C-ABI call.  The tensors
@@ -183,13 +185,14 @@ class PreparedCall:
                 raise TypeError("page_table must be int32")
             _need(page_table, -(-(start_pos + T) // page_size), "page_table")
         _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
+        out_dt = DTYPE_CODES[_dtype_of(out)]
         ws_ptr, ws_bytes = None, 0
         if workspace is not None:
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         head = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
                 v_cache.data_ptr(), kv_head_stride)
-        tail = (out.data_ptr(), out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim,
-                window, ws_ptr, ws_bytes, _stream(stream))
+        tail = (out.data_ptr(), out_row_stride, out_dt, T, start_pos, num_heads, num_kv_heads,
+                head_dim, window, ws_ptr, ws_bytes, _stream(stream))
         if start_pos_dev is not None:
             # start_pos is the largest the device value may take
             import torch
@@ -200,7 +203,7 @@ class PreparedCall:
             self._args = (DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
                           v_cache.data_ptr(), int(page_size),
                           k_cache.numel() // (page_size * num_kv_heads * head_dim),
-                          page_table.data_ptr(), out.data_ptr(), out_row_stride, T,
+                          page_table.data_ptr(), out.data_ptr(), out_row_stride, out_dt, T,
                           start_pos_dev.data_ptr(), start_pos, num_heads, num_kv_heads, head_dim,
                           window, ws_ptr, ws_bytes, _stream(stream))
         elif page_table is not None:
@@ -227,7 +230,8 @@ class PreparedCall:
 def prefill_attn_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                     start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
                     stream=None):
-    """Strided call; workspace is a device tensor (any dtype) or None."""
+    """Strided call; workspace is a device tensor (any dtype) or None; out is
+    float32, bfloat16 or float16."""
     return PreparedCall(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                         start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream)()
 

@@ -77,7 +77,8 @@ struct Params {
     const void *q;
     const void *k;
     const void *v;
-    float *out;
+    void *out;        // [T] rows of out_row_stride elements of out_dtype
+    int out_dtype;    // PA_DTYPE_F32, or BF16 / F16 (rounded to nearest even)
     float *ws_o;      // [S][T*H][D] split partials, normalised by their own l
     float2 *ws_ml;    // [S][T*H]    (running max of raw scores, l)
     int64_t q_row_stride, kv_head_stride, out_row_stride;
@@ -150,6 +151,34 @@ struct F16 {
         return __builtin_bit_cast(uint32_t, v);
     }
 };
+
+// Four consecutive outputs of one row at element e of out: fp32 (ODT
+// PA_DTYPE_F32), or rounded to the nearest even bf16 / fp16.  Written once and
+// not read again by the call: non-temporal stores keep them from displacing
+// cached K/V lines.
+template <int ODT>
+__device__ inline void store_out4(void *out, int64_t e, f32x4 v) {
+    if constexpr (ODT == PA_DTYPE_F32) {
+        __builtin_nontemporal_store(v, (f32x4 *)((float *)out + e));
+    } else {
+        const u32x2 x = ODT == PA_DTYPE_BF16
+                            ? u32x2{Bf16::pack(v[0], v[1]), Bf16::pack(v[2], v[3])}
+                            : u32x2{F16::pack(v[0], v[1]), F16::pack(v[2], v[3])};
+        __builtin_nontemporal_store(x, (u32x2 *)((uint16_t *)out + e));
+    }
+}
+
+// f(std::integral_constant<int, out_dtype>) for the call's output type, so
+// that a row's stores are one branch-free run of the type's instructions.
+template <class F>
+__device__ inline void with_out_dtype(int out_dtype, F &&f) {
+    if (out_dtype == PA_DTYPE_BF16)
+        f(std::integral_constant<int, PA_DTYPE_BF16>{});
+    else if (out_dtype == PA_DTYPE_F16)
+        f(std::integral_constant<int, PA_DTYPE_F16>{});
+    else
+        f(std::integral_constant<int, PA_DTYPE_F32>{});
+}
 
 // ---- work-group -> (query tile, kv head, split) ----------------------------
 
@@ -242,17 +271,17 @@ __device__ inline void write_rows(const Params &p, const Tile &w, const Rows &r,
     if (!r.ok) return;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (p.S == 1) {
-        // written once and not read again by this call: non-temporal stores keep
-        // the output from displacing cached K/V lines
-        float *dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g;
+        const int64_t e = (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g;
+        with_out_dtype(p.out_dtype, [&](auto ODT_) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                f32x4 val = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv,
-                             o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
-                __builtin_nontemporal_store(val, (f32x4 *)(dst + 32 * db + 8 * r4));
-            }
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    f32x4 val = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv,
+                                 o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv};
+                    store_out4<decltype(ODT_)::value>(p.out, e + 32 * db + 8 * r4, val);
+                }
+        });
     } else {
         const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
         float *dst = p.ws_o + row * D + 4 * g;
@@ -1164,12 +1193,14 @@ void attn_fwd16_r16(Params p) {
     if (r.ok && (KSPLIT == 1 || half == 0)) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         if (p.S == 1) {
-            float *dst = p.out + (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+            const int64_t e = (int64_t)r.t * p.out_row_stride + (int64_t)r.h * D + 4 * g4;
+            with_out_dtype(p.out_dtype, [&](auto ODT_) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                __builtin_nontemporal_store(
-                    f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv},
-                    (f32x4 *)(dst + 16 * db));
+                for (int db = 0; db < NDB; ++db)
+                    store_out4<decltype(ODT_)::value>(
+                        p.out, e + 16 * db,
+                        f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv});
+            });
         } else {
             const int64_t row = (int64_t)w.split * p.T * p.H + (int64_t)r.t * p.H + r.h;
             float *dst = p.ws_o + row * D + 4 * g4;
@@ -1349,8 +1380,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
 // m* the largest m_s among splits that saw a valid key (l_s > 0).
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const float2 *ws_ml,
-                                                    float *out, int64_t out_row_stride, int T, int H,
-                                                    int S, float c) {
+                                                    void *out, int out_dtype, int64_t out_row_stride,
+                                                    int T, int H, int S, float c) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t rows = (int64_t)T * H;
     const int64_t row = idx / (D / 4);
@@ -1372,8 +1403,10 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
         }
     }
     const int t = (int)(row / H), h = (int)(row % H);
-    __builtin_nontemporal_store(acc * (1.f / wsum),
-                                (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
+    const int64_t e = (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4;
+    with_out_dtype(out_dtype, [&](auto ODT_) {
+        store_out4<decltype(ODT_)::value>(out, e, acc * (1.f / wsum));
+    });
 }
 
 // The same merge for many splits (short chunks over long caches): one
@@ -1384,8 +1417,8 @@ __global__ __launch_bounds__(256) void merge_splits(const float *ws_o, const flo
 // LDS.
 template <int D>
 __global__ __launch_bounds__(512) void merge_splits_wide(const float *ws_o, const float2 *ws_ml,
-                                                         float *out, int64_t out_row_stride, int T,
-                                                         int H, int S) {
+                                                         void *out, int out_dtype,
+                                                         int64_t out_row_stride, int T, int H, int S) {
     constexpr int C4 = D / 4, NG = 512 / C4;
     __shared__ float wts[512];
     __shared__ float red[512 / kWave];
@@ -1431,8 +1464,10 @@ __global__ __launch_bounds__(512) void merge_splits_wide(const float *ws_o, cons
     if (g == 0) {
         for (int i = 1; i < NG; ++i) acc += part[i * C4 + d4];
         const int t = (int)(row / H), h = (int)(row % H);
-        __builtin_nontemporal_store(acc * (1.f / wsum),
-                                    (f32x4 *)(out + (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4));
+        const int64_t e = (int64_t)t * out_row_stride + (int64_t)h * D + 4 * d4;
+        with_out_dtype(out_dtype, [&](auto ODT_) {
+            store_out4<decltype(ODT_)::value>(out, e, acc * (1.f / wsum));
+        });
     }
 }
 
@@ -1507,8 +1542,8 @@ const Variant kVariants[] = {
     {PA_DTYPE_F32, 256, 32, 1, kThreads, kRowsPerGroup, 1, attn_fwd32<256, 32>, attn_fwd32<256, 32>, attn_fwd32<256, 32>, nullptr},
 };
 
-using MergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int, float);
-using WideMergeFn = void (*)(const float *, const float2 *, float *, int64_t, int, int, int);
+using MergeFn = void (*)(const float *, const float2 *, void *, int, int64_t, int, int, int, float);
+using WideMergeFn = void (*)(const float *, const float2 *, void *, int, int64_t, int, int, int);
 
 // splits above which the merge reads them in parallel (merge_splits_wide)
 constexpr int kWideMergeSplits = 8;
@@ -1689,8 +1724,8 @@ struct CacheLayout {
 };
 
 int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const void *k,
-           const void *v, int64_t kv_head_stride, const CacheLayout &lay, float *out,
-           int64_t out_row_stride, int T, int start_pos, int H, int KVH, int D, int window, void *ws,
+           const void *v, int64_t kv_head_stride, const CacheLayout &lay, void *out,
+           int64_t out_row_stride, int out_dtype, int T, int start_pos, int H, int KVH, int D, int window, void *ws,
            hipStream_t stream) {
     const int ring = lay.ring;
     Params p;
@@ -1698,6 +1733,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.k = k;
     p.v = v;
     p.out = out;
+    p.out_dtype = out_dtype;
     p.ws_o = pl.S > 1 ? (float *)((char *)ws + pl.ws_o_offset) : nullptr;
     p.ws_ml = pl.S > 1 ? (float2 *)((char *)ws + pl.ws_ml_offset) : nullptr;
     p.vop = pl.var->pack ? (const uint16_t *)ws : nullptr;
@@ -1736,14 +1772,14 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     if (pl.S > kWideMergeSplits) {
         hipLaunchKernelGGL(wide_merge_for(D), dim3((unsigned)((int64_t)T * H)), dim3(512), 0, stream,
-                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_row_stride, T, H,
-                           pl.S);
+                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_dtype,
+                           out_row_stride, T, H, pl.S);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     } else if (pl.S > 1) {
         const int64_t n = (int64_t)T * H * (D / 4);
         hipLaunchKernelGGL(merge_for(D), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, stream,
-                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_row_stride, T, H,
-                           pl.S, p.c);
+                           (const float *)p.ws_o, (const float2 *)p.ws_ml, out, out_dtype,
+                           out_row_stride, T, H, pl.S, p.c);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     }
     return PA_OK;
@@ -1752,8 +1788,9 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
 // rows_per_head: the rows the kernels address in each kv head's block (L for
 // a linear cache, the slot count of a ring).
 int check_args(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
-               int64_t kv_head_stride, int64_t rows_per_head, const float *out,
-               int64_t out_row_stride, int T, int start_pos, int H, int KVH, int D, int window) {
+               int64_t kv_head_stride, int64_t rows_per_head, const void *out,
+               int64_t out_row_stride, int out_dtype, int T, int start_pos, int H, int KVH, int D,
+               int window) {
     if (!q || !k || !v || !out) return PA_ERR_INVALID_ARG;
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st == PA_ERR_INVALID_ARG) return st;
@@ -1765,7 +1802,10 @@ int check_args(int dtype, const void *q, int64_t q_row_stride, const void *k, co
     // the 16-bit kernels address one kv head's rows with 32-bit buffer offsets
     if (dtype != PA_DTYPE_F32 && rows_per_head * D * eb > kMaxHeadBytes) return PA_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_UNSUPPORTED;
-    if ((q_row_stride * eb) % 16 || (kv_head_stride * eb) % 16 || (out_row_stride * 4) % 16)
+    if (out_dtype != PA_DTYPE_F32 && out_dtype != PA_DTYPE_BF16 && out_dtype != PA_DTYPE_F16)
+        return PA_ERR_UNSUPPORTED;
+    // outputs go out in groups of four elements of a row (16 or 8 bytes)
+    if ((q_row_stride * eb) % 16 || (kv_head_stride * eb) % 16 || out_row_stride % 4)
         return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
@@ -1808,8 +1848,8 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
                int start_pos, int H, int KVH, int D, int window, void *stream) {
     const int64_t row = (int64_t)H * D;
     const int64_t kvs = ((int64_t)start_pos + T) * D;
-    int st = check_args(dtype, q, row, k, v, kvs, (int64_t)start_pos + T, out, row, T, start_pos, H,
-                        KVH, D, window);
+    int st = check_args(dtype, q, row, k, v, kvs, (int64_t)start_pos + T, out, row, PA_DTYPE_F32, T,
+                        start_pos, H, KVH, D, window);
     if (st != PA_OK) return st;
     Plan pl;
     st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
@@ -1817,14 +1857,15 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
     void *ws = nullptr;
     st = scratch_for(pl.ws_bytes, &ws);
     if (st != PA_OK) return st;
-    return launch(pl, dtype, q, row, k, v, kvs, CacheLayout{}, out, row, T, start_pos, H, KVH, D,
+    return launch(pl, dtype, q, row, k, v, kvs, CacheLayout{}, out, row, PA_DTYPE_F32, T, start_pos,
+                  H, KVH, D,
                   window, ws, (hipStream_t)stream);
 }
 
 // Plan, workspace check and launch of the strided entry points (arguments checked).
 int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const void *v,
-           int64_t kv_head_stride, const CacheLayout &lay, float *out, int64_t out_row_stride,
-           int T, int start_pos, int H, int KVH, int D, int window, void *workspace,
+           int64_t kv_head_stride, const CacheLayout &lay, void *out, int64_t out_row_stride,
+           int out_dtype, int T, int start_pos, int H, int KVH, int D, int window, void *workspace,
            size_t workspace_bytes, void *stream) {
     Plan pl;
     const int st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl, lay.start_pos_dev != nullptr);
@@ -1833,7 +1874,7 @@ int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const 
         if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
     }
-    return launch(pl, dtype, q, q_row_stride, k, v, kv_head_stride, lay, out, out_row_stride, T,
+    return launch(pl, dtype, q, q_row_stride, k, v, kv_head_stride, lay, out, out_row_stride, out_dtype, T,
                   start_pos, H, KVH, D, window, workspace, (hipStream_t)stream);
 }
 
@@ -1865,27 +1906,27 @@ int prefill_attn_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
 }
 
 int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_cache,
-                    const void *v_cache, int64_t kv_head_stride, float *out,
-                    int64_t out_row_stride, int T, int start_pos, int num_heads,
+                    const void *v_cache, int64_t kv_head_stride, void *out,
+                    int64_t out_row_stride, int out_dtype, int T, int start_pos, int num_heads,
                     int num_kv_heads, int head_dim, int window, void *workspace,
                     size_t workspace_bytes, void *stream) {
     int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride,
-                        (int64_t)start_pos + T, out, out_row_stride, T, start_pos, num_heads,
+                        (int64_t)start_pos + T, out, out_row_stride, out_dtype, T, start_pos, num_heads,
                         num_kv_heads, head_dim, window);
     if (st != PA_OK) return st;
     return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
-                  out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+                  out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
 }
 
 int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_ring,
-                         const void *v_ring, int64_t kv_head_stride, int ring_slots, float *out,
-                         int64_t out_row_stride, int T, int start_pos, int num_heads,
+                         const void *v_ring, int64_t kv_head_stride, int ring_slots, void *out,
+                         int64_t out_row_stride, int out_dtype, int T, int start_pos, int num_heads,
                          int num_kv_heads, int head_dim, int window, void *workspace,
                          size_t workspace_bytes, void *stream) {
     if (ring_slots < 1) return PA_ERR_INVALID_ARG;
     int st = check_args(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_slots, out,
-                        out_row_stride, T, start_pos, num_heads, num_kv_heads, head_dim, window);
+                        out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window);
     if (st != PA_OK) return st;
     // the ring must hold every key the chunk reads at once: the window before
     // the chunk's first query through its last key
@@ -1896,21 +1937,21 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const v
     CacheLayout lay;
     lay.ring = ring_slots >= L ? 0 : (int)ring_slots;
     return run_ex(dtype, q, q_row_stride, k_ring, v_ring, kv_head_stride, lay, out, out_row_stride,
-                  T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
+                  out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
 }
 
 int prefill_attn_paged_dev_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_pool,
                               const void *v_pool, int page_size, int num_pages,
-                              const int32_t *page_table, float *out, int64_t out_row_stride, int T,
-                              const int32_t *start_pos_dev, int max_start_pos, int num_heads,
+                              const int32_t *page_table, void *out, int64_t out_row_stride,
+                              int out_dtype, int T, const int32_t *start_pos_dev, int max_start_pos, int num_heads,
                               int num_kv_heads, int head_dim, int window, void *workspace,
                               size_t workspace_bytes, void *stream) {
     if (!start_pos_dev) return PA_ERR_INVALID_ARG;
     if (!page_table || num_pages < 1) return PA_ERR_INVALID_ARG;
     if (page_size < 64 || (page_size & (page_size - 1)) != 0) return PA_ERR_UNSUPPORTED;
     int st = check_args(dtype, q, q_row_stride, k_pool, v_pool, (int64_t)page_size * head_dim,
-                        page_size, out, out_row_stride, T, max_start_pos, num_heads, num_kv_heads,
+                        page_size, out, out_row_stride, out_dtype, T, max_start_pos, num_heads, num_kv_heads,
                         head_dim, window);
     if (st != PA_OK) return st;
     CacheLayout lay;
@@ -1918,15 +1959,15 @@ int prefill_attn_paged_dev_ex(int dtype, const void *q, int64_t q_row_stride, co
     lay.page_shift = __builtin_ctz((unsigned)page_size);
     lay.num_pages = num_pages;
     lay.start_pos_dev = start_pos_dev;
-    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, T,
+    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, out_dtype, T,
                   max_start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
 }
 
 int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_pool,
                           const void *v_pool, int page_size, int num_pages,
-                          const int32_t *page_table, float *out, int64_t out_row_stride, int T,
-                          int start_pos, int num_heads, int num_kv_heads, int head_dim, int window,
+                          const int32_t *page_table, void *out, int64_t out_row_stride,
+                          int out_dtype, int T, int start_pos, int num_heads, int num_kv_heads, int head_dim, int window,
                           void *workspace, size_t workspace_bytes, void *stream) {
     if (!page_table || num_pages < 1) return PA_ERR_INVALID_ARG;
     // a page holds whole KV tiles of every kernel (64 keys at most)
@@ -1934,14 +1975,15 @@ int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride, const 
     // the pool's pages as the head stride of a linear cache of num_pages*page_size
     // rows: the shape and pointer checks are those of prefill_attn_ex
     int st = check_args(dtype, q, q_row_stride, k_pool, v_pool, (int64_t)page_size * head_dim,
-                        page_size, out, out_row_stride, T, start_pos, num_heads, num_kv_heads,
+                        page_size, out, out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads,
                         head_dim, window);
     if (st != PA_OK) return st;
     CacheLayout lay;
     lay.page_table = page_table;
     lay.page_shift = __builtin_ctz((unsigned)page_size);
     lay.num_pages = num_pages;
-    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, T, start_pos,
+    return run_ex(dtype, q, q_row_stride, k_pool, v_pool, 0, lay, out, out_row_stride, out_dtype, T,
+                  start_pos,
                   num_heads, num_kv_heads, head_dim, window, workspace, workspace_bytes, stream);
 }
 

@@ -29,18 +29,22 @@
  *            `capacity` positions passes kv_head_stride = capacity*head_dim
  *            to prefill_attn_ex; rows L .. capacity-1 are never read, so
  *            they may hold anything, NaN included.
- *   out      (t, h, d)  at out[t*out_row_stride + h*head_dim + d], fp32;
+ *   out      (t, h, d)  at out[t*out_row_stride + h*head_dim + d];
  *            packed entry points: out_row_stride = num_heads*head_dim.
  *
  * Storage types: fp32, bf16 or fp16 for q/k/v (bf16 and fp16 passed as
- * uint16_t bit patterns), fp32 for out.  bf16/fp16 inputs are multiplied on
- * the matrix cores with fp32 accumulation; the softmax runs in fp32.
+ * uint16_t bit patterns).  out is fp32 (the page's bf16 workload keeps an
+ * fp32 output; the packed entry points always write fp32); the strided forms
+ * take out_dtype, a PA_DTYPE_* value, and then write the fp32 result rounded
+ * to the nearest even bf16 or fp16 for a caller whose next step reads 16-bit
+ * activations.  bf16/fp16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; the softmax runs in fp32.
  *
  * Supported shapes: head_dim in {32, 64, 128, 256, 512} for bf16/fp16 and
  * {32, 64, 128, 256} for fp32; any T >= 1, start_pos >= 0, num_heads a
  * multiple of num_kv_heads with num_heads/num_kv_heads <= 128.  Pointers must
- * be 16-byte aligned and q_row_stride, kv_head_stride and out_row_stride
- * must keep every row 16-byte aligned.
+ * be 16-byte aligned, q_row_stride and kv_head_stride must keep every row
+ * 16-byte aligned and out_row_stride must be a multiple of 4 elements.
  *
  * Ownership: every pointer is caller-owned device memory.  The library keeps
  * no pointer after a call returns, never frees caller memory, only reads q,
@@ -70,7 +74,8 @@ extern "C" {
 #define PA_ERR_INVALID_ARG 1   /* null pointer, T < 1, start_pos < 0, heads < 1,
                                   num_heads % num_kv_heads != 0, window < 0,
                                   a stride below its minimum                      */
-#define PA_ERR_UNSUPPORTED 2   /* head_dim, dtype, group size or alignment       */
+#define PA_ERR_UNSUPPORTED 2   /* head_dim, dtype, out_dtype, group size or
+                                  alignment                                       */
 #define PA_ERR_HIP 3           /* a HIP runtime call or launch failed             */
 #define PA_ERR_WORKSPACE 4     /* workspace missing or smaller than required      */
 
@@ -101,7 +106,10 @@ int prefill_attn_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
 
 /*
  * General form: explicit strides (in elements) and an explicit workspace.
- * dtype is a PA_DTYPE_* value.  workspace may be NULL when
+ * dtype is a PA_DTYPE_* value, the storage type of q, k_cache and v_cache;
+ * out_dtype, a PA_DTYPE_* value too, is out's (any of the three with any
+ * dtype; the split-KV partials in the workspace stay fp32 whatever it is).
+ * workspace may be NULL when
  * prefill_attn_workspace_bytes() returns 0 for the same arguments; otherwise
  * it must be device memory of at least that many bytes, 256-byte aligned,
  * and it must not be used by anything else until the work enqueued by this
@@ -109,7 +117,7 @@ int prefill_attn_f16(const uint16_t *q, const uint16_t *k_cache, const uint16_t 
  */
 int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride,
                     const void *k_cache, const void *v_cache, int64_t kv_head_stride,
-                    float *out, int64_t out_row_stride,
+                    void *out, int64_t out_row_stride, int out_dtype,
                     int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
                     int window, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -131,7 +139,7 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride,
  */
 int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride,
                          const void *k_ring, const void *v_ring, int64_t kv_head_stride,
-                         int ring_slots, float *out, int64_t out_row_stride,
+                         int ring_slots, void *out, int64_t out_row_stride, int out_dtype,
                          int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
                          int window, void *workspace, size_t workspace_bytes, void *stream);
 
@@ -153,8 +161,8 @@ int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride,
  */
 int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride,
                           const void *k_pool, const void *v_pool, int page_size, int num_pages,
-                          const int32_t *page_table, float *out, int64_t out_row_stride,
-                          int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                          const int32_t *page_table, void *out, int64_t out_row_stride,
+                          int out_dtype, int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
                           int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -169,8 +177,8 @@ int prefill_attn_paged_ex(int dtype, const void *q, int64_t q_row_stride,
  */
 int prefill_attn_paged_dev_ex(int dtype, const void *q, int64_t q_row_stride,
                               const void *k_pool, const void *v_pool, int page_size, int num_pages,
-                              const int32_t *page_table, float *out, int64_t out_row_stride,
-                              int T, const int32_t *start_pos_dev, int max_start_pos,
+                              const int32_t *page_table, void *out, int64_t out_row_stride,
+                              int out_dtype, int T, const int32_t *start_pos_dev, int max_start_pos,
                               int num_heads, int num_kv_heads, int head_dim, int window,
                               void *workspace, size_t workspace_bytes, void *stream);
 

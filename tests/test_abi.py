@@ -25,6 +25,37 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+def _header_signatures():
+    """{name: [parameter declarations]} of the functions the header declares."""
+    import re
+    text = open(binding.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    sigs = {}
+    for name, params in re.findall(r"\b(prefill_\w+)\s*\(([^)]*)\)\s*;", text):
+        sigs[name] = [p.strip() for p in params.split(",") if p.strip() and p.strip() != "void"]
+    return sigs
+
+
+def test_binding_matches_header_signatures(lib):
+    """Every declared function is bound with as many arguments as the header
+    gives it, and each pointer, 64-bit and size_t parameter has a matching
+    ctypes type (a parameter added to the ABI but not to the binding fails here)."""
+    sigs = _header_signatures()
+    assert set(sigs) == set(pa.header_functions())
+    for name, params in sigs.items():
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None and len(argtypes) == len(params), (name, params, argtypes)
+        for decl, ct in zip(params, argtypes):
+            if "*" in decl:
+                assert ct in (ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)), (name, decl, ct)
+            elif decl.startswith("int64_t"):
+                assert ct is ctypes.c_int64, (name, decl, ct)
+            elif decl.startswith("size_t"):
+                assert ct is ctypes.c_size_t, (name, decl, ct)
+            else:
+                assert decl.startswith("int ") and ct is ctypes.c_int, (name, decl, ct)
+
+
 def test_strerror(lib):
     for code in range(5):
         assert pa.strerror(code) not in ("", "unknown status")
@@ -66,17 +97,22 @@ def test_unsupported(lib, fn):
 def test_ex_strides_and_workspace(lib):
     ex = lib.prefill_attn_ex
     # strides below their minimum
-    assert ex(1, FAKE, 100, FAKE, FAKE, 64 * 10, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
-    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 9, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
-    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 10, FAKE, 127, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
-    # unknown dtype
-    assert ex(7, FAKE, 128, FAKE, FAKE, 640, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    assert ex(1, FAKE, 100, FAKE, FAKE, 64 * 10, FAKE, 128, 0, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 9, FAKE, 128, 0, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    assert ex(1, FAKE, 128, FAKE, FAKE, 64 * 10, FAKE, 127, 0, 4, 6, 2, 2, 64, 0, None, 0, None) == 1
+    # unknown dtype, unknown output dtype
+    assert ex(7, FAKE, 128, FAKE, FAKE, 640, FAKE, 128, 0, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    assert ex(1, FAKE, 128, FAKE, FAKE, 640, FAKE, 128, 3, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    assert ex(1, FAKE, 128, FAKE, FAKE, 640, FAKE, 128, -1, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
     # a row stride that breaks 16-byte alignment of rows
-    assert ex(1, FAKE, 132, FAKE, FAKE, 640, FAKE, 128, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    assert ex(1, FAKE, 132, FAKE, FAKE, 640, FAKE, 128, 0, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
+    # an output row stride that is not a multiple of 4 elements, for any output type
+    for od in (0, 1, 2):
+        assert ex(1, FAKE, 128, FAKE, FAKE, 640, FAKE, 130, od, 4, 6, 2, 2, 64, 0, None, 0, None) == 2
     # a split plan without (or with too little) workspace
     need = pa.workspace_bytes("bf16", 64, 8000, 8, 8, 128)
     assert need > 0
-    args = (1, FAKE, 8 * 128, FAKE, FAKE, 8064 * 128, FAKE, 8 * 128, 64, 8000, 8, 8, 128, 0)
+    args = (1, FAKE, 8 * 128, FAKE, FAKE, 8064 * 128, FAKE, 8 * 128, 1, 64, 8000, 8, 8, 128, 0)
     assert ex(*args, None, 0, None) == pa.PA_ERR_WORKSPACE
     assert ex(*args, FAKE, need - 1, None) == pa.PA_ERR_WORKSPACE
     assert ex(*args, FAKE + 16, need, None) == pa.PA_ERR_WORKSPACE   # not 256-byte aligned
@@ -131,7 +167,7 @@ def test_ring_arguments(lib):
 
     def call(ring, kvs=None, w=W, t=T, s=sp, dtype=1):
         kvs = ring * D if kvs is None else kvs
-        return rx(dtype, FAKE, H * D, FAKE, FAKE, kvs, ring, FAKE, H * D, t, s, H, KVH, D, w,
+        return rx(dtype, FAKE, H * D, FAKE, FAKE, kvs, ring, FAKE, H * D, 0, t, s, H, KVH, D, w,
                   None, 0, None)
 
     assert call(0) == E
@@ -175,8 +211,8 @@ def test_paged_arguments(lib):
     E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
     H, KVH, D = 8, 2, 128
 
-    def call(P=256, npages=10, table=FAKE, T=4, sp=1000, w=0, dtype=1, q=FAKE):
-        return px(dtype, q, H * D, FAKE, FAKE, P, npages, table, FAKE, H * D, T, sp, H, KVH, D, w,
+    def call(P=256, npages=10, table=FAKE, T=4, sp=1000, w=0, dtype=1, q=FAKE, od=0):
+        return px(dtype, q, H * D, FAKE, FAKE, P, npages, table, FAKE, H * D, od, T, sp, H, KVH, D, w,
                   None, 0, None)
 
     assert call(table=None) == E
@@ -186,6 +222,7 @@ def test_paged_arguments(lib):
     assert call(q=None) == E
     assert call(dtype=5) == U
     assert call(q=FAKE + 2) == U
+    assert call(od=4) == U
 
 
 def test_paged_dev_arguments(lib):
@@ -196,8 +233,8 @@ def test_paged_dev_arguments(lib):
     H, KVH, D = 8, 2, 128
 
     def call(sp_dev=FAKE, maxsp=1000, P=256, table=FAKE, T=4):
-        return px(1, FAKE, H * D, FAKE, FAKE, P, 10, table, FAKE, H * D, T, sp_dev, maxsp, H, KVH, D, 0,
-                  None, 0, None)
+        return px(1, FAKE, H * D, FAKE, FAKE, P, 10, table, FAKE, H * D, 0, T, sp_dev, maxsp, H, KVH,
+                  D, 0, None, 0, None)
 
     assert call(sp_dev=None) == E
     assert call(table=None) == E
