@@ -372,7 +372,9 @@ template <int N>
 __device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_bytes,
                                    const int (&lin)[N], int (&off)[N]) {
     const int s0 = j0 % p.ring;
-    if (p.ring % BK == 0 && j0 + BK <= p.L) {
+    // (in 64 bits: a last tile may end at 2^31)
+    const bool past = (int64_t)j0 + BK > p.L;
+    if (p.ring % BK == 0 && !past) {
 #pragma unroll
         for (int i = 0; i < N; ++i) off[i] = lin[i];
         return s0 * row_bytes;
@@ -389,7 +391,7 @@ __device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_byte
             off[i] = ((s0 + row) % p.ring) * row_bytes + (lin[i] - row * row_bytes);
         }
     }
-    if (j0 + BK > p.L) {
+    if (past) {
         const int end = (p.L - j0) * row_bytes;
 #pragma unroll
         for (int i = 0; i < N; ++i) off[i] = lin[i] >= end ? kPastRange : off[i];
@@ -414,7 +416,8 @@ __device__ inline void paged_rsrc(const Params &p, int kvh, int j0, int row_byte
 }
 
 // The page of the tile whose first key is j (paged caches), -1 past L.
-__device__ inline int page_of(const Params &p, int j) {
+// (j in 64 bits: the tile after the last one may start at 2^31)
+__device__ inline int page_of(const Params &p, int64_t j) {
     return j < p.L ? p.page_table[j >> p.page_shift] : -1;
 }
 #endif
@@ -681,7 +684,7 @@ void attn_fwd16(Params p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     pv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], soff, 0, 0);
             }
-            pg_next = page_of(p, (kt + 1) * BK);     // one tile ahead of its use
+            pg_next = page_of(p, (int64_t)(kt + 1) * BK);     // one tile ahead of its use
         } else {
             int ko[LOADS], vo[LOADS];
             const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
@@ -985,7 +988,7 @@ void attn_fwd16_r16(Params p) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         pv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], soff, 0, 0);
             }
-            pg_next = page_of(p, (kt + 1) * BK);     // one tile ahead of its use
+            pg_next = page_of(p, (int64_t)(kt + 1) * BK);     // one tile ahead of its use
         } else {
             // the operand-ordered V copy is linear in the call's tiles; K (and
             // V read in place) come from the ring slots

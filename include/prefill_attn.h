@@ -17,6 +17,10 @@
  *   softmax of the valid scores weights the value rows:
  *       out_t = sum_j softmax(s)_j * v_j                      (Step 3)
  *   Masked keys contribute exactly nothing.  window <= 0 means no window.
+ *   (Keys are loaded in tiles of 32 or 64 positions: the cache rows of keys
+ *   [0, L) that share a tile with a row's band are read and weighted by 0,
+ *   so they must hold finite values, as every written cache does; tiles
+ *   outside every row's band and rows past L are never read.)
  *
  * Layouts (all element offsets, row-major; same page, "Layout"):
  *   q        (t, h, d)  at q[t*q_row_stride + h*head_dim + d]

@@ -118,6 +118,21 @@ def test_ex_strides_and_workspace(lib):
     assert ex(*args, FAKE + 16, need, None) == pa.PA_ERR_WORKSPACE   # not 256-byte aligned
 
 
+def test_head_size_limit(lib):
+    """The 16-bit kernels address one kv head's rows with 32-bit buffer
+    offsets: a cache with one row per head more than 0x7FE00000 bytes hold is
+    refused before anything is enqueued (fp32 caches are addressed in 64 bits)."""
+    D = 128
+    rows = 0x7FE00000 // (D * 2)
+    L = rows + 1
+    for dtype in (1, 2):
+        assert lib.prefill_attn_ex(dtype, FAKE, 4 * D, FAKE, FAKE, L * D, FAKE, 4 * D, 0, 64, L - 64, 4,
+                                   1, D, 0, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+    # the same shape in fp32 passes the shape checks (here it stops at the workspace)
+    assert lib.prefill_attn_ex(0, FAKE, 4 * D, FAKE, FAKE, L * D, FAKE, 4 * D, 0, 64, L - 64, 4,
+                               1, D, 0, None, 0, None) == pa.PA_ERR_WORKSPACE
+
+
 def test_plan_shapes():
     p = pa.plan("bf16", 2048, 6144, 32, 8, 128)
     assert p["tokens_per_tile"] * 4 == 128 and p["query_tiles"] == 64
