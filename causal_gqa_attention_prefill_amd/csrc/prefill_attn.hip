@@ -359,26 +359,21 @@ constexpr int kMaxHeadBytes = 0x7FE00000;
 constexpr int kPastRange = 0x7FF00000;
 
 // Ring cache (sliding-window layers): key j of a kv head sits in slot
-// j % ring.  lin[i] is the offset lane load i of a tile would have in a
-// linear cache, row * row_bytes + chunk; the function sets off[i] and returns
-// the scalar offset that go with it for the tile whose first key is j0.
-// When the ring is a multiple of the tile and the tile ends before L, the
-// tile's rows sit in consecutive slots from s0 = j0 % ring: the linear
-// offsets plus s0 rows.  Otherwise each row finds its slot s0 + row, wrapped
-// once past the ring's end (rings of at least BK slots; the wrap test
-// compares lin itself, since chunk < row_bytes) or reduced by division, and
-// rows at keys >= L read as zero, like the rows past L of a linear cache.
+// j % ring.  When the ring is a multiple of the tile and the tile ends before
+// L (ring_tile_linear), the tile's rows sit in consecutive slots from
+// s0 = j0 % ring: the linear offsets with s0 rows added as the scalar offset.
+// Otherwise ring_offsets: lin[i] is the offset lane load i of the tile would
+// have in a linear cache, row * row_bytes + chunk; each row finds its slot
+// s0 + row, wrapped once past the ring's end (rings of at least BK slots; the
+// wrap test compares lin itself, since chunk < row_bytes) or reduced by
+// division, and rows at keys >= L read as zero, like the rows past L of a
+// linear cache.  s0 is kept by the caller (ring_advance).
+[[maybe_unused]] __device__ inline bool ring_tile_linear(const Params &p, int j0, int BK) {
+    return p.ring % BK == 0 && j0 <= p.L - BK;   // j0 + BK <= L without forming it (may be 2^31)
+}
 template <int N>
-__device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_bytes,
-                                   const int (&lin)[N], int (&off)[N]) {
-    const int s0 = j0 % p.ring;
-    // (in 64 bits: a last tile may end at 2^31)
-    const bool past = (int64_t)j0 + BK > p.L;
-    if (p.ring % BK == 0 && !past) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) off[i] = lin[i];
-        return s0 * row_bytes;
-    }
+__device__ inline void ring_offsets(const Params &p, int j0, int s0, int BK, int row_bytes,
+                                    const int (&lin)[N], int (&off)[N]) {
     if (p.ring >= BK) {
         const int wrap_at = (p.ring - s0) * row_bytes, base = s0 * row_bytes;
         const int back = p.ring * row_bytes;
@@ -391,12 +386,18 @@ __device__ inline int ring_offsets(const Params &p, int j0, int BK, int row_byte
             off[i] = ((s0 + row) % p.ring) * row_bytes + (lin[i] - row * row_bytes);
         }
     }
-    if (past) {
+    if (j0 > p.L - BK) {
         const int end = (p.L - j0) * row_bytes;
 #pragma unroll
         for (int i = 0; i < N; ++i) off[i] = lin[i] >= end ? kPastRange : off[i];
     }
-    return 0;
+}
+
+// Slot of the first key of the next tile: a wavefront issues its tiles in
+// order, so the slot moves by BK modulo the ring instead of a division per tile.
+[[maybe_unused]] __device__ inline int ring_advance(int s, int BK, int ring) {
+    const int n = s + BK;
+    return n < ring ? n : ring >= BK ? n - ring : n % ring;
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -658,6 +659,7 @@ void attn_fwd16(Params p) {
     const float c = p.c;
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
+    int ring_s = 0;     // ring caches: slot of the next tile's first key
     auto issue = [&](int kt, int kdst, int vdst) {
         // LDS destination (M0) of this wave's chunks: one scalar base, made
         // opaque at every issue so that the compiler derives the per-chunk
@@ -686,15 +688,27 @@ void attn_fwd16(Params p) {
             }
             pg_next = page_of(p, (int64_t)(kt + 1) * BK);     // one tile ahead of its use
         } else {
-            int ko[LOADS], vo[LOADS];
-            const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
-            const int vs = ring_offsets(p, kt * BK, BK, D * 2, voff, vo);
+            const int s0 = ring_s, j0 = kt * BK;
+            ring_s = ring_advance(ring_s, BK, p.ring);
+            if (ring_tile_linear(p, j0, BK)) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_ADDR(mb + kdst + i * 1024), 16, ko[i], ks, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_ADDR(mb + vdst + i * 1024), 16, vo[i], vs, 0, 0);
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], s0 * D * 2, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], s0 * D * 2, 0, 0);
+                }
+            } else {
+                int ko[LOADS], vo[LOADS];
+                ring_offsets(p, j0, s0, BK, D * 2, koff, ko);
+                ring_offsets(p, j0, s0, BK, D * 2, voff, vo);
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_ADDR(mb + kdst + i * 1024), 16, ko[i], 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_ADDR(mb + vdst + i * 1024), 16, vo[i], 0, 0, 0);
+                }
             }
         }
     };
@@ -797,6 +811,7 @@ void attn_fwd16(Params p) {
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
     if (kb0 < ke) {
         if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
+        if constexpr (LAYOUT == kRing) ring_s = kb0 * BK % p.ring;
         issue(kb0, B0K::value, B0V::value);
         wait_vmem();
         __syncthreads();
@@ -960,6 +975,7 @@ void attn_fwd16_r16(Params p) {
     const float c = p.c;
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
+    int ring_s = 0;     // ring caches: slot of the next tile's first key
     auto issue = [&](int kt, int kdst, int vdst) {
         if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
@@ -992,17 +1008,30 @@ void attn_fwd16_r16(Params p) {
         } else {
             // the operand-ordered V copy is linear in the call's tiles; K (and
             // V read in place) come from the ring slots
-            int ko[LOADS], vo[LOADS];
-            const int ks = ring_offsets(p, kt * BK, BK, D * 2, koff, ko);
-            int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : 0;
-            if constexpr (!VPACK) vbase_t = ring_offsets(p, kt * BK, BK, D * 2, voff, vo);
+            const int s0 = ring_s, j0 = kt * BK;
+            ring_s = ring_advance(ring_s, BK, p.ring);
+            const int vpack_base = (kt - p.vop_kt_lo) * TILE_BYTES;
+            if (ring_tile_linear(p, j0, BK)) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, ko[i], ks, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, VPACK ? voff[i] : vo[i],
-                    vbase_t, 0, 0);
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], s0 * D * 2, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i],
+                        VPACK ? vpack_base : s0 * D * 2, 0, 0);
+                }
+            } else {
+                int ko[LOADS], vo[LOADS];
+                ring_offsets(p, j0, s0, BK, D * 2, koff, ko);
+                if constexpr (!VPACK) ring_offsets(p, j0, s0, BK, D * 2, voff, vo);
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, ko[i], 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, VPACK ? voff[i] : vo[i],
+                        VPACK ? vpack_base : 0, 0, 0);
+                }
             }
         }
     };
@@ -1118,6 +1147,7 @@ void attn_fwd16_r16(Params p) {
     if constexpr (KSPLIT == 1) {
         if (kb0 < ke) {
             if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
+            if constexpr (LAYOUT == kRing) ring_s = kb0 * BK % p.ring;
             issue(kb0, B0K::value, B0V::value);
             wait_vmem();
             __syncthreads();
@@ -1142,6 +1172,7 @@ void attn_fwd16_r16(Params p) {
         const int he = half == 0 ? kb0 + niter : ke;
         if (niter > 0) {
             if constexpr (LAYOUT == kPaged) pg_next = hb < he ? page_of(p, hb * BK) : -1;
+            if constexpr (LAYOUT == kRing) ring_s = hb * BK % p.ring;
             if (hb < he) issue(hb, B0K::value, B0V::value);
             wait_vmem();
             __syncthreads();
