@@ -139,6 +139,11 @@ struct Bf16 {
         bf16x2 v = {(__bf16)lo, (__bf16)hi};
         return __builtin_bit_cast(uint32_t, v);
     }
+    // both halves times c, rounded to nearest even
+    __device__ static inline uint32_t scale2(uint32_t x, float c) {
+        const bf16x2 v = __builtin_bit_cast(bf16x2, x);
+        return pack((float)v[0] * c, (float)v[1] * c);
+    }
 };
 
 struct F16 {
@@ -149,6 +154,10 @@ struct F16 {
     __device__ static inline uint32_t pack(float lo, float hi) {
         f16x2 v = {(_Float16)lo, (_Float16)hi};
         return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ static inline uint32_t scale2(uint32_t x, float c) {
+        const f16x2 v = __builtin_bit_cast(f16x2, x);
+        return pack((float)v[0] * c, (float)v[1] * c);
     }
 };
 
@@ -649,6 +658,12 @@ void attn_fwd16(Params p) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
             qreg[ks] = r.ok ? *(const u32x4 *)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+        // Q * log2(e)/sqrt(D), rounded to the storage type: the products
+        // then deliver scores in log2 units
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qreg[ks][e] = Ty::scale2(qreg[ks][e], p.c);
     }
 
     f32x16 o[D / 32];
@@ -656,7 +671,12 @@ void attn_fwd16(Params p) {
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
     float mref = -INFINITY;          // reference row max, log2 units (raw score * c)
     float lsum = 0.f;                // this lane's share of the row sum
-    const float c = p.c;
+    // The score chains start from -mref (0 while mref is -inf), so each
+    // product chain ends at s*c - mref, the exponent itself; zc holds that
+    // start in every accumulator slot and changes only when mref moves.
+    float zval = 0.f;
+    f32x16 zc = f32x16{};
+    float thr = -INFINITY;           // move mref when the tile max (minus mref) passes this
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
     int ring_s = 0;     // ring caches: slot of the next tile's first key
@@ -720,7 +740,7 @@ void attn_fwd16(Params p) {
         if (!r.wave_any || j0 > r.w_pos_max || j0 + BK - 1 < r.w_lo_min) return;
         f32x16 s[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+        for (int b = 0; b < NB; ++b) s[b] = zc;
         {
             // S^T = K Q^T: the NB chains interleaved, operand reads S_AHEAD
             // products ahead of the matrix core
@@ -768,17 +788,28 @@ void attn_fwd16(Params p) {
                 mt0 = max3(mt0, s[b][i], s[b][i + 1]);
                 mt1 = max3(mt1, s[b][i + 2], s[b][i + 3]);
             }
-        float mt = max_halves_swap(fmaxf(mt0, mt1)) * c;
-        // move the reference max only when p could exceed 2^8 (exact either way)
-        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
-            const float mnew = fmaxf(mref, mt);
-            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-            mref = mnew;
-            lsum *= alpha;
+        const float mt = max_halves_swap(fmaxf(mt0, mt1));
+        // move the reference max only when p could exceed 2^8 (exact either
+        // way), or for the first keys a row sees
+        if (__builtin_amdgcn_ballot_w64(mt > thr) != 0) {
+            const float mnew = fmaxf(mref, mt - zval);
+            if (mnew != -INFINITY) {
+                const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+                const float shift = zval + mnew;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) s[b][i] -= shift;
+                mref = mnew;
+                zval = -mnew;
+                thr = kRescaleLog2;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zc[i] = zval;
+            }
         }
-        const float mc = mref == -INFINITY ? 0.f : mref;
         u32x4 pb[BK / 16];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -787,8 +818,8 @@ void attn_fwd16(Params p) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int i0 = 8 * half + 2 * jj;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][i0], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][i0 + 1], c, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(s[b][i0]);
+                    const float p1 = __builtin_amdgcn_exp2f(s[b][i0 + 1]);
                     const uint32_t pk = Ty::pack(p0, p1);
                     pb[2 * b + half][jj] = pk;
                     lsum = Ones::dot(pk, lsum, Ty{});
@@ -887,6 +918,7 @@ template <class Ty, int D, int BK, bool VPACK, int KSPLIT, int LAYOUT>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd16_r16(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+    constexpr bool SEED = D < 512;   // scores start from -mref (see below)
     take_device_start(p);
     static_assert(D >= 128 && D % 32 == 0 && BK % 32 == 0, "tile shape");
     static_assert(KSPLIT == 1 || (KSPLIT == 2 && !VPACK), "key halves read V in place");
@@ -966,12 +998,26 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             qreg[ks] = r.ok ? *(const u32x4 *)(qp + 32 * ks) : u32x4{0, 0, 0, 0};
+        // Q * log2(e)/sqrt(D), rounded to the storage type: the products
+        // then deliver scores in log2 units
+        if constexpr (SEED) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qreg[ks][e] = Ty::scale2(qreg[ks][e], p.c);
+        }
     }
 
     f32x4v o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x4v{0.f, 0.f, 0.f, 0.f};
     float mref = -INFINITY, lsum = 0.f;
+    // SEED: the score chains start from -mref (0 while mref is -inf), so each
+    // chain ends at the exponent s*c - mref; zc changes only when mref moves.
+    // Otherwise (head_dim 512, where four more registers would spill) the
+    // chains start from 0 and one FMA per score applies the scale and max.
+    float zval = 0.f, thr = -INFINITY;
+    f32x4v zc = f32x4v{0.f, 0.f, 0.f, 0.f};
     const float c = p.c;
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
@@ -1045,7 +1091,7 @@ void attn_fwd16_r16(Params p) {
         // ahead than in the 32-row kernel)
         f32x4v s[NSB];
 #pragma unroll
-        for (int b = 0; b < NSB; ++b) s[b] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NSB; ++b) s[b] = zc;
         {
             constexpr int NS = NSB * NKS, S_AHEAD = 6;
             u32x4 ka[NS];
@@ -1077,8 +1123,8 @@ void attn_fwd16_r16(Params p) {
             mt0 = max3(mt0, s[b][0], s[b][1]);
             mt1 = max3(mt1, s[b][2], s[b][3]);
         }
-        const float mt = max_halves_swap(max_quarters_swap(fmaxf(mt0, mt1))) * c;
-        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
+        const float mt = max_halves_swap(max_quarters_swap(fmaxf(mt0, mt1))) * (SEED ? 1.f : c);
+        if (!SEED && __builtin_amdgcn_ballot_w64(mt > mref + kRescaleLog2) != 0) {
             const float mnew = fmaxf(mref, mt);
             const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
             mref = mnew;
@@ -1086,7 +1132,25 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         }
-        const float mc = mref == -INFINITY ? 0.f : mref;
+        if (SEED && __builtin_amdgcn_ballot_w64(mt > thr) != 0) {
+            const float mnew = fmaxf(mref, mt - zval);
+            if (mnew != -INFINITY) {
+                const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+                const float shift = zval + mnew;
+#pragma unroll
+                for (int b = 0; b < NSB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[b][i] -= shift;
+                mref = mnew;
+                zval = -mnew;
+                thr = kRescaleLog2;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+                zc = f32x4v{zval, zval, zval, zval};
+            }
+        }
+        const float mc = SEED || mref == -INFINITY ? 0.f : mref;
         u32x4 pb[BK / 32];
 #pragma unroll
         for (int kp = 0; kp < BK / 32; ++kp)
@@ -1095,8 +1159,8 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const f32x4v &sb = s[2 * kp + half];
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[2 * jj], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[2 * jj + 1], c, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(SEED ? sb[2 * jj] : fmaf(sb[2 * jj], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(SEED ? sb[2 * jj + 1] : fmaf(sb[2 * jj + 1], c, -mc));
                     const uint32_t pk = Ty::pack(p0, p1);
                     pb[kp][2 * half + jj] = pk;
                     lsum = Ones::dot(pk, lsum, Ty{});
