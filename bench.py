@@ -115,6 +115,76 @@ def cpu_baseline(wl, x, target_s: float):
                       f"({rows} per chunk), fp64 oracle, {t:.1f} s wall, {f / 1e9:.1f} GFLOP"}
 
 
+def sample_device(step, sync, samples: int = 3, load_s: float = 1.0, timeout_s: float = 30.0):
+    """GPU clocks and socket power read by amd-smi while the workload runs.
+
+    The workload first runs for load_s seconds; then amd-smi runs as a child
+    process `samples` times in a row while steps keep being launched, so every
+    reading is taken under load.  Returns the readings (None when the tool is
+    missing or its output cannot be read).
+    """
+    import shutil
+    import subprocess
+    # under a profiler the child would inherit its tool library: no sample
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+
+    def run_for(cond):
+        n = 0
+        while cond():
+            for _ in range(10):
+                step()
+            sync()
+            n += 10
+        return n
+
+    t0 = time.perf_counter()
+    n = run_for(lambda: time.perf_counter() - t0 < load_s)
+    readings = []
+    for _ in range(samples):
+        try:
+            proc = subprocess.Popen([exe, "metric", "-g", "0", "-p", "-c", "--json"],
+                                    stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            return None
+        t1 = time.perf_counter()
+        n += run_for(lambda: proc.poll() is None and time.perf_counter() - t1 < timeout_s)
+        if proc.poll() is None:
+            proc.kill()
+        try:
+            out, _ = proc.communicate(timeout=5)
+        except subprocess.TimeoutExpired:
+            return None
+        rec = parse_amd_smi(out)
+        if rec is None:
+            return None
+        readings.append(rec)
+    clocks = [r["gfx_clock_mhz_mean"] for r in readings]
+    return {"gfx_clock_mhz_mean": clocks, "socket_power_w": [r["socket_power_w"] for r in readings],
+            "gfx_clock_mhz_last": readings[-1]["gfx_clock_mhz"],
+            "sampled_by": f"amd-smi metric -p -c, {samples} readings under load ({n} steps in "
+                          f"{time.perf_counter() - t0:.1f} s)"}
+
+
+def parse_amd_smi(text: str):
+    """Per-die gfx clocks (MHz) and socket power (W) from `amd-smi metric -p -c
+    --json` output, or None."""
+    try:
+        starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
+        rec = json.loads(text[min(starts):])
+        gpu = rec["gpu_data"][0] if isinstance(rec, dict) else rec[0]
+        clocks = [gpu["clock"][k]["clk"]["value"] for k in sorted(gpu["clock"]) if k.startswith("gfx_")]
+        power = gpu["power"]["socket_power"]["value"]
+        return {"gfx_clock_mhz": clocks,
+                "gfx_clock_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+                "socket_power_w": power}
+    except (ValueError, KeyError, IndexError, TypeError):
+        return None
+
+
 def calibrate_copy(nbytes: int):
     """A copy kernel of known size: FETCH_SIZE / WRITE_SIZE per dispatch of this
     kernel, divided by nbytes, is the factor that turns the counters into bytes."""
@@ -215,6 +285,8 @@ def main():
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-device-sample", action="store_true",
+                    help="skip reading GPU clocks and power with amd-smi after the timed steps")
     ap.add_argument("--kv-write", action="store_true",
                     help="time the KV cache write of the workload's chunks (prefill_kv_write) "
                          "instead of the attention; HBM-bound, priced against 8 TB/s")
@@ -384,6 +456,8 @@ def main():
         gbs = bytes_step / len(calls) / (mean_launch_ms * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS,
                               "unit": "GB/s", "frac": round(gbs / HBM_GBS, 4), "traffic": traffic}
+    # clocks and power under the same load (after the timed region, outside it)
+    result["device"] = None if args.no_device_sample else sample_device(step, torch.cuda.synchronize)
     if wl.ring:
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:

@@ -60,3 +60,18 @@ def test_inputs_are_seeded_and_rounded():
 def test_bench_refuses_several_gpus():
     p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_parse_amd_smi():
+    gpu = {"gpu": 0,
+           "power": {"socket_power": {"value": 1012, "unit": "W"}, "gfx_voltage": "N/A"},
+           "clock": {**{f"gfx_{i}": {"clk": {"value": 2000 + 10 * i, "unit": "MHz"},
+                                     "max_clk": {"value": 2400, "unit": "MHz"}} for i in range(8)},
+                     "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}
+    text = "warning line\n" + json.dumps({"gpu_data": [gpu]})
+    rec = bench.parse_amd_smi(text)
+    assert rec["gfx_clock_mhz"] == [2000 + 10 * i for i in range(8)]
+    assert rec["gfx_clock_mhz_mean"] == 2035.0 and rec["socket_power_w"] == 1012
+    assert bench.parse_amd_smi(json.dumps([gpu]))["socket_power_w"] == 1012
+    assert bench.parse_amd_smi("no output") is None
+    assert bench.parse_amd_smi(json.dumps({"gpu_data": [{"gpu": 0}]})) is None
