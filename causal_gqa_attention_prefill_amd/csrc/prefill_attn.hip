@@ -19,9 +19,13 @@
 //                 row r -> token t0 + r / G, head kvh*G + r % G, so the G
 //                 query heads that share kv head kvh share every K/V tile
 //   per KV tile of BK keys (only tiles that intersect some row's band):
-//     global -> LDS: K tile as [key][d], V tile transposed to [d][key]
+//     global -> LDS: K and V tiles as [key][d] (DMA, no register staging);
+//                   V is read back transposed (or, at head_dim 512, from a
+//                   per-call copy in MFMA operand order)
 //     S^T = K Q^T   on MFMA (32x32 tiles, keys on M, rows on N); Q stays in
-//                   registers for the whole loop
+//                   registers for the whole loop, pre-scaled by
+//                   log2(e)/sqrt(head_dim), and each chain starts at minus
+//                   the row's reference max, so scores come out as exponents
 //     mask          only on tiles that cut some row's band (index compares)
 //     online softmax in fp32: each lane holds one row's scores for 16 keys
 //                   per 32-key block, so the row max needs one exchange
