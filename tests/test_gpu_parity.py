@@ -57,20 +57,48 @@ def test_largest_groups(orc, dtype, D, H, KVH, T, sp, W):
     assert_parity(got, ref, dtype, f"group {H // KVH} {dtype} D{D}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_peaked_softmax(orc, dtype):
-    """Q scaled up 16x: peaked rows, large running-max jumps and rescales."""
-    H, KVH, D, T, sp = 8, 2, 128, 150, 420
+@pytest.mark.parametrize("dtype,D", [("f32", 128), ("bf16", 128), ("f16", 128), ("bf16", 256), ("f16", 256)])
+def test_peaked_softmax(orc, dtype, D):
+    """Q scaled up 16x: peaked rows, large running-max jumps and rescales (the
+    reference max moves on later tiles too, shifting scores already computed)."""
+    H, KVH, T, sp = 8, 2, 150, 420
     x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=11, dtype=dtype)
     q16 = x.q_f32 * np.float32(16.0)
     if dtype == "bf16":
         q_store = workloads.round_to_bf16_bits(q16)
         q16 = workloads.bf16_bits_to_f32(q_store)
+    elif dtype == "f16":
+        h = q16.astype(np.float16)
+        q_store, q16 = h.view(np.uint16), h.astype(np.float32)
     else:
         q_store = q16
     got = run_packed(x, T, sp, H, KVH, D, 0, q_rows=q_store)
     ref = orc.attention(q16, x.k_f32, x.v_f32, T, sp, H, KVH, D)
-    assert_parity(got, ref, dtype, f"{dtype} Qx16")
+    assert_parity(got, ref, dtype, f"{dtype} D{D} Qx16")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 128), ("bf16", 256)])
+def test_late_running_max_jump(orc, dtype, D):
+    """One key far into each row's range gets a score well above everything
+    before it, so the reference max moves late in the key loop and every
+    earlier contribution is rescaled; rows see it or not by the causal bound."""
+    H, KVH, T, sp = 8, 2, 96, 700
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=23, dtype=dtype)
+    qh = x.q_f32.reshape(T, H, D)
+    k = x.k_f32.copy()
+    j = sp + 40                                   # rows t >= 40 see this key
+    for kh in range(KVH):
+        k[kh, j] = 6.0 * np.sign(qh[50, kh * (H // KVH)])
+    if dtype == "bf16":
+        k_store = workloads.round_to_bf16_bits(k)
+        k = workloads.bf16_bits_to_f32(k_store)
+    else:
+        h = k.astype(np.float16)
+        k_store, k = h.view(np.uint16), h.astype(np.float32)
+    x.k_store, x.k_f32 = k_store, k
+    got = run_packed(x, T, sp, H, KVH, D, 0)
+    ref = orc.attention(x.q_f32, k, x.v_f32, T, sp, H, KVH, D)
+    assert_parity(got, ref, dtype, f"{dtype} D{D} late max jump")
 
 
 def test_planted_keys_outside_band(orc):
