@@ -81,11 +81,12 @@ def read_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, x, target_s: float):
-    """The fp64 oracle on the host cores, on sampled rows of the same chunks."""
+def cpu_baseline(wl, x, target_s: float, threads: int | None = None):
+    """The fp64 oracle on the host cores (all of them unless threads is given),
+    on sampled rows of the same chunks."""
     import oracle
     orc = oracle.default()
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
     rng = np.random.default_rng(12345)
 
@@ -284,6 +285,8 @@ def main():
                          f"{WARMUP_S} s of work, so that the GPU has left its idle clocks)")
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="oracle threads for the CPU baseline (default: every visible core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-device-sample", action="store_true",
                     help="skip reading GPU clocks and power with amd-smi after the timed steps")
@@ -463,7 +466,7 @@ def main():
     if wl.page_size:
         result["config"]["page_size"] = wl.page_size
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.cpu_threads)
     print(json.dumps(result), flush=True)
 
 
