@@ -293,6 +293,10 @@ def test_workload_mistral_bf16_chunked(orc):
     _run_workload(orc, "mistral_bf16_chunked")
 
 
+def test_workload_mistral_f16_chunked(orc):
+    _run_workload(orc, "mistral_f16_chunked")
+
+
 def test_workload_gemma_global_bf16(orc):
     _run_workload(orc, "gemma_global_bf16", n_random=32)
 

@@ -68,6 +68,11 @@ WORKLOADS = {
         "mistral_bf16_chunked", "bf16", 32, 8, 128, 0,
         ((2048, 0), (2048, 2048), (2048, 4096), (2048, 6144)), 8192, 0.5, 103,
         "Mistral-7B-shaped bf16 prefill of an 8192-token prompt as four T=2048 chunks"),
+    # the same prompt, shapes and values with fp16 storage (the fp16 matrix path)
+    "mistral_f16_chunked": Workload(
+        "mistral_f16_chunked", "f16", 32, 8, 128, 0,
+        ((2048, 0), (2048, 2048), (2048, 4096), (2048, 6144)), 8192, 0.5, 103,
+        "Mistral-7B-shaped fp16 prefill of an 8192-token prompt as four T=2048 chunks"),
     "gemma_global_bf16": Workload(
         "gemma_global_bf16", "bf16", 8, 2, 512, 0, ((2048, 61440),), 63488, 0.3, 104,
         "Gemma-style global layer, 8/2 heads, head_dim 512, T=2048 at start_pos 61440"),
