@@ -93,6 +93,7 @@ struct Params {
     int n_items;      // nq * KVH * S work-groups
     float c;          // log2(e) / sqrt(head_dim)
     int order;        // 1: within a die, longest query tiles first then shortest first; 0: longest first
+    int pair;         // 1: each work-group holds two query tiles of one kv head (8 wavefronts)
     int kv_bytes;     // bytes of the L valid rows (linear) or of the ring slots of one kv head
     int L;            // keys of the call: start_pos + T
     int ring;         // ring cache: key j sits in slot j % ring of its kv head; 0: row j
@@ -237,6 +238,34 @@ __device__ inline Tile locate(const Params &p) {
     w.kt_begin = min(ke, kb + w.split * per);
     w.kt_end = min(ke, w.kt_begin + per);
     return w;
+}
+
+// Paired work-groups (causal, no window, no key split): item -> (kv head, j);
+// wavefronts 0..3 take the long query tile nq-1-j, wavefronts 4..7 the short
+// one j (none when they coincide, odd nq).  The short tile's keys are a prefix
+// of the long one's, so the work-group steps through the long tile's KV range
+// and every tile both need comes into LDS once instead of once per
+// work-group; the short tile's wavefronts skip the tiles past their rows.
+// Returns the group's tile; kb/ke get the work-group's KV range.
+template <int BK>
+__device__ inline Tile locate_pair(const Params &p, int grp, int &kb, int &ke) {
+    const int item = xcd_logical_item(blockIdx.x, p.n_items);
+    const int np = (p.nq + 1) / 2;
+    const int j = item % np, kvh = item / np;
+    const int ql = p.nq - 1 - j, qs = j;
+    const int tl0 = ql * p.TQ, tl1 = min(tl0 + p.TQ, p.T) - 1;
+    const int ts0 = qs * p.TQ, ts1 = min(ts0 + p.TQ, p.T) - 1;
+    // union of the two KV ranges (the short tile's rows end no later than the long one's)
+    kb = min(first_key(p.start_pos + tl0, p.window), first_key(p.start_pos + ts0, p.window)) / BK;
+    ke = (p.start_pos + tl1) / BK + 1;
+    Tile t;
+    t.kvh = kvh;
+    t.split = 0;
+    t.t0 = grp == 0 ? tl0 : ts0;
+    t.t_last = grp == 0 ? tl1 : (qs == ql ? -1 : ts1);     // odd nq: the middle tile alone
+    t.kt_begin = kb;
+    t.kt_end = ke;
+    return t;
 }
 
 // Per-lane row and per-wave token range.
@@ -611,8 +640,16 @@ void attn_fwd16(Params p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches, M0
     const int l32 = lane & 31, g = lane >> 5;
-    const Tile w = locate<BK>(p);
-    const Rows r = rows_of(p, w, wave, l32);
+    int kb_all = 0, ke_all = 0;      // the work-group's KV tiles
+    Tile w;
+    if (NW == 8 && p.pair) {
+        w = locate_pair<BK>(p, wave >> 2, kb_all, ke_all);
+    } else {
+        w = locate<BK>(p);
+        kb_all = w.kt_begin;
+        ke_all = w.kt_end;
+    }
+    const Rows r = rows_of(p, w, (NW == 8 && p.pair) ? (wave & 3) : wave, l32);
     const __amdgpu_buffer_rsrc_t rk =
         head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
     const __amdgpu_buffer_rsrc_t rv =
@@ -839,7 +876,7 @@ void attn_fwd16(Params p) {
         });
     };
 
-    const int kb0 = w.kt_begin, ke = w.kt_end;
+    const int kb0 = kb_all, ke = ke_all;
     using B0K = std::integral_constant<int, 0>;
     using B1K = std::integral_constant<int, TILE_BYTES>;
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
@@ -1616,7 +1653,8 @@ struct Variant {
     int threads;               // work-group size (4 or 8 wavefronts)
     int rows;                  // (token, head) rows per work-group
     int ksplit;                // 2: the tile's keys are split between two wavefront halves;
-                               // 0: variant without the V operand-order copy, for few query tiles
+                               // 0: variant without the V operand-order copy, for few query tiles;
+                               // 3: two query tiles per work-group sharing their KV tiles
     KernelFn fn;               // linear caches
     KernelFn fn_ring;          // ring caches (key j in slot j % ring)
     KernelFn fn_paged;         // paged caches (key j in page page_table[j / page_size])
@@ -1627,6 +1665,7 @@ const Variant kVariants[] = {
     {PA_DTYPE_BF16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 32, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 32, 64, 4, 2, kRing>, attn_fwd16<Bf16, 32, 64, 4, 2, kPaged>, nullptr},
     {PA_DTYPE_BF16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 64, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 64, 64, 4, 2, kRing>, attn_fwd16<Bf16, 64, 64, 4, 2, kPaged>, nullptr},
     {PA_DTYPE_BF16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<Bf16, 128, 64, 4, 2, kLinear>, attn_fwd16<Bf16, 128, 64, 4, 2, kRing>, attn_fwd16<Bf16, 128, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_BF16, 128, 64, 1, 2 * kThreads, kRowsPerGroup, 3, attn_fwd16<Bf16, 128, 64, 8, 2, kLinear>, attn_fwd16<Bf16, 128, 64, 8, 2, kRing>, attn_fwd16<Bf16, 128, 64, 8, 2, kPaged>, nullptr},
     {PA_DTYPE_BF16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 256, 64, false, 1, kLinear>, attn_fwd16_r16<Bf16, 256, 64, false, 1, kRing>, attn_fwd16_r16<Bf16, 256, 64, false, 1, kPaged>, nullptr},
     {PA_DTYPE_BF16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<Bf16, 256, 32, false, 2, kLinear>, attn_fwd16_r16<Bf16, 256, 32, false, 2, kRing>, attn_fwd16_r16<Bf16, 256, 32, false, 2, kPaged>, nullptr},
     {PA_DTYPE_BF16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<Bf16, 512, 32, true, 1, kLinear>, attn_fwd16_r16<Bf16, 512, 32, true, 1, kRing>, attn_fwd16_r16<Bf16, 512, 32, true, 1, kPaged>, pack_v_operands<512, 32, true>},
@@ -1634,6 +1673,7 @@ const Variant kVariants[] = {
     {PA_DTYPE_F16, 32, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 32, 64, 4, 2, kLinear>, attn_fwd16<F16, 32, 64, 4, 2, kRing>, attn_fwd16<F16, 32, 64, 4, 2, kPaged>, nullptr},
     {PA_DTYPE_F16, 64, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 64, 64, 4, 2, kLinear>, attn_fwd16<F16, 64, 64, 4, 2, kRing>, attn_fwd16<F16, 64, 64, 4, 2, kPaged>, nullptr},
     {PA_DTYPE_F16, 128, 64, 2, kThreads, kRowsPerGroup, 1, attn_fwd16<F16, 128, 64, 4, 2, kLinear>, attn_fwd16<F16, 128, 64, 4, 2, kRing>, attn_fwd16<F16, 128, 64, 4, 2, kPaged>, nullptr},
+    {PA_DTYPE_F16, 128, 64, 1, 2 * kThreads, kRowsPerGroup, 3, attn_fwd16<F16, 128, 64, 8, 2, kLinear>, attn_fwd16<F16, 128, 64, 8, 2, kRing>, attn_fwd16<F16, 128, 64, 8, 2, kPaged>, nullptr},
     {PA_DTYPE_F16, 256, 64, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 256, 64, false, 1, kLinear>, attn_fwd16_r16<F16, 256, 64, false, 1, kRing>, attn_fwd16_r16<F16, 256, 64, false, 1, kPaged>, nullptr},
     {PA_DTYPE_F16, 256, 32, 1, kThreads16, kRowsPerGroup / 2, 2, attn_fwd16_r16<F16, 256, 32, false, 2, kLinear>, attn_fwd16_r16<F16, 256, 32, false, 2, kRing>, attn_fwd16_r16<F16, 256, 32, false, 2, kPaged>, nullptr},
     {PA_DTYPE_F16, 512, 32, 1, kThreads16, kRowsPerGroup, 1, attn_fwd16_r16<F16, 512, 32, true, 1, kLinear>, attn_fwd16_r16<F16, 512, 32, true, 1, kRing>, attn_fwd16_r16<F16, 512, 32, true, 1, kPaged>, pack_v_operands<512, 32, true>},
@@ -1781,7 +1821,18 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     pl->TQ = var->rows / pl->G;
     pl->nq = (int)cdiv(T, pl->TQ);
     pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq);
-    const int64_t items = (int64_t)pl->nq * KVH * pl->S;
+    // Causal tiles without a window and without key splits, on a grid that
+    // fills every resident slot: the long and the short query tile of a kv
+    // head go into one work-group whose wavefront groups share the KV tiles
+    // of the common key prefix (same rows per group, so the tile size and the
+    // plan above stay valid; on a smaller grid the pair would only slow the
+    // long tile down).
+    if (pl->S == 1 && pl->nq >= 2 && (int64_t)pl->nq * KVH >= (int64_t)kCus * var->groups_per_cu &&
+        (window == 0 || (int64_t)window >= (int64_t)start_pos + T))
+        if (const Variant *alt = find_ksplit_variant(dtype, D, 3))
+            if (alt->rows == var->rows) var = pl->var = alt;
+    const int64_t items = var->ksplit == 3 ? (int64_t)((pl->nq + 1) / 2) * KVH
+                                           : (int64_t)pl->nq * KVH * pl->S;
     if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
     pl->items = (int)items;
     int64_t tiles = 0;
@@ -1856,6 +1907,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.n_items = pl.items;
     p.c = (float)(1.4426950408889634 / sqrt((double)D));
     p.order = pl.var->groups_per_cu == 2 ? 1 : 0;
+    p.pair = pl.var->ksplit == 3;
     p.L = start_pos + T;
     p.ring = ring;
     p.page_table = lay.page_table;

@@ -225,7 +225,10 @@ size_t prefill_attn_workspace_bytes(int dtype, int T, int start_pos, int num_hea
  *   [2] KV splits per tile (1: no split)     [3] work-groups launched
  *   [4] keys per KV tile                     [5] wavefronts per work-group
  *   [6] workspace bytes                      [7] KV tiles visited in total
- * and returns PA_OK or the status the same call would return.
+ * and returns PA_OK or the status the same call would return.  At head_dim
+ * 128 with 16-bit inputs, a causal call without a window whose query tiles
+ * fill the GPU holds two query tiles per work-group (8 wavefronts, [3] =
+ * ceil([1] / 2) * num_kv_heads); [7] still counts each query tile's visits.
  */
 int prefill_attn_plan(int dtype, int T, int start_pos, int num_heads, int num_kv_heads,
                       int head_dim, int window, int64_t *info, int n);

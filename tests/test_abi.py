@@ -136,8 +136,14 @@ def test_head_size_limit(lib):
 def test_plan_shapes():
     p = pa.plan("bf16", 2048, 6144, 32, 8, 128)
     assert p["tokens_per_tile"] * 4 == 128 and p["query_tiles"] == 64
-    assert p["workgroups"] == 64 * 8 * p["kv_splits"]
-    assert p["waves_per_workgroup"] in (4, 8)
+    # a full causal grid without a window pairs the long and the short query
+    # tile of each kv head in one eight-wavefront work-group
+    assert p["kv_splits"] == 1 and p["waves_per_workgroup"] == 8 and p["workgroups"] == 32 * 8
+    # a window (or a grid that leaves CUs idle) keeps one query tile per work-group
+    pw = pa.plan("bf16", 2048, 6144, 32, 8, 128, 1000)
+    assert pw["workgroups"] == 64 * 8 * pw["kv_splits"] and pw["waves_per_workgroup"] == 4
+    ps = pa.plan("bf16", 256, 0, 32, 8, 128)
+    assert ps["workgroups"] == 8 * 8 * ps["kv_splits"] and ps["waves_per_workgroup"] == 4
     # every (tile, kv head) visits only KV tiles that hold a valid key of one of its rows
     bk = p["keys_per_tile"]
     tiles = 0
