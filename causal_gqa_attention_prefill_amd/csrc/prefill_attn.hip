@@ -18,6 +18,9 @@
 //   work-group  = 4 wavefronts = 128 (token, head) rows of one GQA group:
 //                 row r -> token t0 + r / G, head kvh*G + r % G, so the G
 //                 query heads that share kv head kvh share every K/V tile
+//                 (at head_dim 128 on a full causal grid: 8 wavefronts, the
+//                 long and the short query tile of the kv head, which share
+//                 the K/V tiles of their common key prefix)
 //   per KV tile of BK keys (only tiles that intersect some row's band):
 //     global -> LDS: K and V tiles as [key][d] (DMA, no register staging);
 //                   V is read back transposed (or, at head_dim 512, from a
