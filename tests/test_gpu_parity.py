@@ -281,6 +281,29 @@ def _run_workload(orc, name, n_random=64):
         assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("dtype,T,sp", [("bf16", 2080, 300), ("f16", 2090, 64), ("bf16", 4096, 0)])
+def test_paired_query_tiles(orc, dtype, T, sp):
+    """Full causal grids pair the long and the short query tile of a kv head in
+    one work-group: an odd tile count (the middle tile alone), a ragged last
+    tile and an unaligned start, against oracle rows from every pair."""
+    import causal_gqa_attention_prefill_amd as pa
+    H, KVH, D = 32, 8, 128
+    plan = pa.plan(dtype, T, sp, H, KVH, D)
+    nq, tq = plan["query_tiles"], plan["tokens_per_tile"]
+    assert plan["waves_per_workgroup"] == 8 and plan["kv_splits"] == 1
+    assert plan["workgroups"] == (nq + 1) // 2 * KVH
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=T + sp, dtype=dtype)
+    got = run_packed(x, T, sp, H, KVH, D, 0)
+    # first and last token of every query tile, for three heads of each kv head
+    ts = sorted({t for q in range(nq) for t in (q * tq, min(q * tq + tq, T) - 1)})
+    heads = [h for kh in range(KVH) for h in (kh * 4, kh * 4 + 3)]
+    rt = np.array([t for t in ts for h in heads[::3]] + [t for t in ts[::7] for h in heads])
+    rh = np.array([h for t in ts for h in heads[::3]] + [h for t in ts[::7] for h in heads])
+    ref = orc.rows(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh)
+    assert_parity(got[rt, rh], ref, dtype, f"paired {dtype} T{T} sp{sp} ({len(rt)} rows)")
+    assert np.isfinite(got).all()
+
+
 def test_workload_tiny_f32(orc):
     _run_workload(orc, "tiny_f32")
 
