@@ -1884,7 +1884,7 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
            int64_t out_row_stride, int out_dtype, int T, int start_pos, int H, int KVH, int D, int window, void *ws,
            hipStream_t stream) {
     const int ring = lay.ring;
-    Params p;
+    Params p{};
     p.q = q;
     p.k = k;
     p.v = v;
