@@ -97,3 +97,38 @@ def test_paged_table_rewritten_between_calls(orc):
         call()
         torch.cuda.synchronize()
         assert_parity(out.cpu().numpy().reshape(T, H, D), ref, dtype, f"table {seed}")
+
+
+@pytest.mark.parametrize("dtype,T,sp,P", [("bf16", 2048, 2048, 256), ("f16", 2080, 700, 64)])
+def test_paged_prefill_paired(orc, dtype, T, sp, P):
+    """A long causal prefill chunk through pages fills the GPU, so the plan
+    pairs the long and the short query tile of each kv head in one
+    work-group (the paged form of the eight-wavefront kernel); sampled rows
+    of every pair against the oracle over the linear cache."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    H, KVH, D = 32, 8, 128
+    plan = pa.plan(dtype, T, sp, H, KVH, D)
+    nq, tq = plan["query_tiles"], plan["tokens_per_tile"]
+    assert plan["waves_per_workgroup"] == 8 and plan["workgroups"] == (nq + 1) // 2 * KVH
+    L = sp + T
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=T + sp, dtype=dtype)
+    npages = -(-L // P) + 5
+    kp, table = workloads.paged_cache(x.k_store, P, L, npages, seed=L, fill=NAN_BITS[dtype])
+    vp, _ = workloads.paged_cache(x.v_store, P, L, npages, seed=L, fill=NAN_BITS[dtype])
+    q = to_device(x.q_store, dtype)
+    out = torch.empty(T, H * D, device=device())
+    nb = pa.workspace_bytes(dtype, T, sp, H, KVH, D, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=device()) if nb else None
+    pa.prefill_attn_paged_ex(q, H * D, to_device(kp, dtype), to_device(vp, dtype), P,
+                             torch.from_numpy(table).to(device()), out, H * D, T, sp, H, KVH, D, 0,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(T, H, D)
+    ts = sorted({t for qi in range(nq) for t in (qi * tq, min(qi * tq + tq, T) - 1)})
+    heads = [kh * 4 + 1 for kh in range(KVH)]
+    rt = np.array([t for t in ts for h in heads])
+    rh = np.array([h for t in ts for h in heads])
+    ref = orc.rows(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh)
+    assert_parity(got[rt, rh], ref, dtype, f"paged paired {dtype} T{T} sp{sp} P{P}")
+    assert np.isfinite(got).all()
