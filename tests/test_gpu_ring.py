@@ -108,3 +108,28 @@ def test_ring_split_plan(orc, dtype, D, R):
     got = _call_ring(x, dtype, x.q_store, kr, vr, R, T, sp, H, KVH, D, W)
     ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, window=W)
     assert_parity(got, ref, dtype, f"ring split {dtype} D{D}")
+
+
+def test_ring_full_causal_paired(orc):
+    """A ring that holds every key (window 0, ring_slots >= L) on a full causal
+    grid: the plan pairs the long and the short query tile of each kv head in
+    one work-group (the ring form of the eight-wavefront kernel); slots past
+    the last key hold NaN and are never read."""
+    import causal_gqa_attention_prefill_amd as pa
+    dtype, H, KVH, D, T, sp = "bf16", 32, 8, 128, 2048, 1000
+    L = sp + T
+    R = L + 77
+    plan = pa.plan(dtype, T, sp, H, KVH, D)
+    nq, tq = plan["query_tiles"], plan["tokens_per_tile"]
+    assert plan["waves_per_workgroup"] == 8 and plan["workgroups"] == (nq + 1) // 2 * KVH
+    x = workloads.make_random(H, KVH, D, T, sp, std=0.5, seed=31, dtype=dtype)
+    kr = workloads.ring_cache(x.k_store, R, L, NAN_BITS[dtype])
+    vr = workloads.ring_cache(x.v_store, R, L, NAN_BITS[dtype])
+    got = _call_ring(x, dtype, x.q_store, kr, vr, R, T, sp, H, KVH, D, 0)
+    ts = sorted({t for qi in range(nq) for t in (qi * tq, min(qi * tq + tq, T) - 1)})
+    heads = [kh * 4 + 2 for kh in range(KVH)]
+    rt = np.array([t for t in ts for h in heads])
+    rh = np.array([h for t in ts for h in heads])
+    ref = orc.rows(x.q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh)
+    assert_parity(got[rt, rh], ref, dtype, "ring paired")
+    assert np.isfinite(got).all()
