@@ -1825,12 +1825,15 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     pl->nq = (int)cdiv(T, pl->TQ);
     pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq);
     // Causal tiles without a window and without key splits, on a grid that
-    // fills every resident slot: the long and the short query tile of a kv
-    // head go into one work-group whose wavefront groups share the KV tiles
-    // of the common key prefix (same rows per group, so the tile size and the
-    // plan above stay valid; on a smaller grid the pair would only slow the
-    // long tile down).
+    // fills every resident slot and whose pairs fit one per CU: the long and
+    // the short query tile of a kv head go into one work-group whose
+    // wavefront groups share the KV tiles of the common key prefix (same rows
+    // per group, so the tile size and the plan above stay valid).  On a
+    // smaller grid the pair would only slow the long tile down; on a larger
+    // one (a second round of work-groups) the fixed pairs lose to the
+    // dispatcher refilling CUs as single tiles finish.
     if (pl->S == 1 && pl->nq >= 2 && (int64_t)pl->nq * KVH >= (int64_t)kCus * var->groups_per_cu &&
+        (int64_t)((pl->nq + 1) / 2) * KVH <= (int64_t)kCus &&
         (window == 0 || (int64_t)window >= (int64_t)start_pos + T))
         if (const Variant *alt = find_ksplit_variant(dtype, D, 3))
             if (alt->rows == var->rows) var = pl->var = alt;

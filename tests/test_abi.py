@@ -144,6 +144,10 @@ def test_plan_shapes():
     assert pw["workgroups"] == 64 * 8 * pw["kv_splits"] and pw["waves_per_workgroup"] == 4
     ps = pa.plan("bf16", 256, 0, 32, 8, 128)
     assert ps["workgroups"] == 8 * 8 * ps["kv_splits"] and ps["waves_per_workgroup"] == 4
+    # more pairs than CUs (a second round): single tiles, refilled by the dispatcher
+    for T in (8192, 2080):
+        pl = pa.plan("bf16", T, 0, 32, 8, 128)
+        assert pl["waves_per_workgroup"] == 4 and pl["workgroups"] == pl["query_tiles"] * 8
     # every (tile, kv head) visits only KV tiles that hold a valid key of one of its rows
     bk = p["keys_per_tile"]
     tiles = 0

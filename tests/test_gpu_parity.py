@@ -281,11 +281,12 @@ def _run_workload(orc, name, n_random=64):
         assert np.isfinite(got).all()
 
 
-@pytest.mark.parametrize("dtype,T,sp", [("bf16", 2080, 300), ("f16", 2090, 64), ("bf16", 4096, 0)])
+@pytest.mark.parametrize("dtype,T,sp", [("bf16", 2048, 300), ("f16", 2040, 64), ("bf16", 2017, 4000)])
 def test_paired_query_tiles(orc, dtype, T, sp):
-    """Full causal grids pair the long and the short query tile of a kv head in
-    one work-group: an odd tile count (the middle tile alone), a ragged last
-    tile and an unaligned start, against oracle rows from every pair."""
+    """Causal grids that fill the GPU with their pairs fitting one per CU pair
+    the long and the short query tile of a kv head in one work-group: an
+    unaligned start, a ragged last tile (8 tokens, 1 token), fp16, against
+    oracle rows from every pair."""
     import causal_gqa_attention_prefill_amd as pa
     H, KVH, D = 32, 8, 128
     plan = pa.plan(dtype, T, sp, H, KVH, D)
@@ -314,6 +315,10 @@ def test_workload_mistral_f32(orc):
 
 def test_workload_mistral_bf16_chunked(orc):
     _run_workload(orc, "mistral_bf16_chunked")
+
+
+def test_workload_mistral_bf16_oneshot(orc):
+    _run_workload(orc, "mistral_bf16_oneshot")
 
 
 def test_workload_mistral_f16_chunked(orc):

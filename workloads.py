@@ -68,6 +68,11 @@ WORKLOADS = {
         "mistral_bf16_chunked", "bf16", 32, 8, 128, 0,
         ((2048, 0), (2048, 2048), (2048, 4096), (2048, 6144)), 8192, 0.5, 103,
         "Mistral-7B-shaped bf16 prefill of an 8192-token prompt as four T=2048 chunks"),
+    # the same prompt in one call (T = 8192 at start_pos 0): the one-shot side
+    # of the chunked == one-shot invariant
+    "mistral_bf16_oneshot": Workload(
+        "mistral_bf16_oneshot", "bf16", 32, 8, 128, 0, ((8192, 0),), 8192, 0.5, 103,
+        "Mistral-7B-shaped bf16 prefill of an 8192-token prompt in one T=8192 call"),
     # the same prompt, shapes and values with fp16 storage (the fp16 matrix path)
     "mistral_f16_chunked": Workload(
         "mistral_f16_chunked", "f16", 32, 8, 128, 0,
