@@ -11,10 +11,16 @@ Output: one JSON line.  ``value`` is attention TFLOP/s over the timed steps
 call.  The ``roofline`` object prices the fused kernel against the dense bf16
 MFMA peak, with the average launch time taken from HIP events on the launch
 stream around the timed steps; ``cpu_baseline`` times the fp64 oracle on a
-bounded sample of the same workload on the host cores.  Diagnostics (per-call
-events over a few extra steps) go to stderr.  Unless --warmup is given, the
-untimed warm-up lasts at least WARMUP_S seconds, long enough for the GPU to
-reach its working clock; the JSON line reports the number of warm-up steps.
+bounded sample of the same workload on the host cores, and compares the GPU
+output of those rows with the oracle's (``parity``).  ``determinism`` reruns
+the step five times after the timed region and compares the outputs bit for
+bit.  Diagnostics (per-call events over a few extra steps) go to stderr.
+
+Warm-up: the --warmup steps (default 10), then more of the same untimed steps
+until at least WARMUP_S seconds of them have run, so that the GPU has left its
+idle clocks before the timed region (from idle it needs some tens of
+milliseconds of load).  The JSON line reports the requested warm-up steps
+(``warmup``) and what actually ran (``warmup_steps_run``, ``warmup_s``).
 """
 from __future__ import annotations
 
@@ -36,7 +42,7 @@ import workloads  # noqa: E402
 METRIC = "prefill attention TFLOP/s and % of MI355X bf16 MFMA peak (T=2048 chunk)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # dense MFMA, MI355X
 HBM_GBS = 8000.0
-WARMUP_S = 0.3
+WARMUP_S = 0.5
 KERNEL_SOURCE = os.path.join(ROOT, "causal_gqa_attention_prefill_amd", "csrc", "prefill_attn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -81,39 +87,76 @@ def read_traffic(workload: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, x, target_s: float, threads: int | None = None):
+# parity bars of the gnosis page (fp32: max |gpu - cpu| <= 1e-4) and of the
+# bf16 / fp16 path, plus relative RMS error bars that a kernel ignoring Q.K^T
+# or shifting the band by one key cannot meet on near-uniform softmax rows
+BAR_MAX_ABS = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
+BAR_REL_RMS = {"f32": 1e-5, "bf16": 5e-3, "f16": 5e-3}
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, x, target_s: float, threads: int | None = None, gpu_out=None):
     """The fp64 oracle on the host cores (all of them unless threads is given),
-    on sampled rows of the same chunks."""
+    on sampled rows of the same chunks.  gpu_out: each chunk's GPU output
+    ([T, H, D] host arrays); the rows the oracle computes are compared with
+    it and the errors returned as a second value."""
     import oracle
     orc = oracle.default()
     threads = threads or oracle.default_threads()
     H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
     rng = np.random.default_rng(12345)
+    diffs, refs = [], []
 
-    def run(rows_per_chunk):
+    def run(rows_per_chunk, keep):
         flops, t_total, n = 0, 0.0, 0
         for ci, (T, sp) in enumerate(wl.chunks):
             _, q_f32 = x.q_rows(ci)
             rt = rng.integers(0, T, rows_per_chunk)
             rh = rng.integers(0, H, rows_per_chunk)
             t0 = time.perf_counter()
-            orc.rows(q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh, window=W,
-                     kv_head_stride=wl.capacity * D, nthreads=threads)
+            ref = orc.rows(q_f32, x.k_f32, x.v_f32, T, sp, H, KVH, D, rt, rh, window=W,
+                           kv_head_stride=wl.capacity * D, nthreads=threads)
             t_total += time.perf_counter() - t0
+            if keep and gpu_out is not None:
+                diffs.append(gpu_out[ci][rt, rh].astype(np.float64) - ref)
+                refs.append(ref)
             pos = sp + rt
             lo = np.maximum(0, pos - W + 1) if W > 0 else np.zeros_like(pos)
             flops += int(4 * D * (pos - lo + 1).sum())
             n += rows_per_chunk
         return flops, t_total, n
 
-    f, t, _ = run(threads * 4)                       # pilot
+    f, t, _ = run(threads * 4, False)                # pilot
     rate = f / max(t, 1e-9)
     per_row = f / (threads * 4 * len(wl.chunks))
     rows = max(threads, int(target_s * rate / per_row / len(wl.chunks)))
-    f, t, n = run(rows)
-    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    f, t, n = run(rows, True)
+    base = {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} (token, head) rows drawn uniformly from the {len(wl.chunks)} chunks "
-                      f"({rows} per chunk), fp64 oracle, {t:.1f} s wall, {f / 1e9:.1f} GFLOP"}
+                      f"({rows} per chunk), fp64 oracle, {t:.1f} s wall, {f / 1e9:.1f} GFLOP",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    parity = None
+    if diffs:
+        d = np.concatenate(diffs)
+        r = np.concatenate(refs)
+        max_abs = float(np.abs(d).max())
+        rel = float(np.sqrt((d ** 2).sum() / (r ** 2).sum()))
+        finite = bool(all(np.isfinite(o).all() for o in gpu_out))
+        parity = {"rows": n, "of": "the rows the CPU baseline computed, GPU output of the last step",
+                  "max_abs": max_abs, "rel_rms": rel, "all_outputs_finite": finite,
+                  "bar_max_abs": BAR_MAX_ABS[wl.dtype], "bar_rel_rms": BAR_REL_RMS[wl.dtype],
+                  "ok": finite and max_abs <= BAR_MAX_ABS[wl.dtype] and rel <= BAR_REL_RMS[wl.dtype]}
+    return base, parity
 
 
 def sample_device(step, sync, samples: int = 3, load_s: float = 1.0, timeout_s: float = 30.0):
@@ -246,8 +289,8 @@ def kv_write_bench(args):
     torch.cuda.synchronize()
     n_warm, t_w = 0, time.perf_counter()
     with torch.cuda.stream(side):
-        while n_warm < max(1, args.warmup or 1) or (args.warmup is None and
-                                                      time.perf_counter() - t_w < WARMUP_S):
+        # replays of the K-step graph: at least one, then until WARMUP_S has passed
+        while n_warm < 1 or time.perf_counter() - t_w < WARMUP_S:
             g.replay()
             side.synchronize()
             n_warm += 1
@@ -280,9 +323,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before the timed ones (default: at least 10 steps and "
-                         f"{WARMUP_S} s of work, so that the GPU has left its idle clocks)")
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps before the timed ones; more of them run until at least "
+                         f"{WARMUP_S} s of work has passed, so that the GPU has left its idle clocks")
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-threads", type=int, default=None,
@@ -374,21 +417,21 @@ def main():
             if events is not None:
                 events[i][1].record()
 
-    # warm-up: from idle the GPU needs some tens of ms of load to reach its
+    # warm-up: the requested steps, then more until WARMUP_S seconds have
+    # passed; from idle the GPU needs some tens of ms of load to reach its
     # working clock (measured: the first 25 steps of the default workload run
-    # ~15% slower than steady state), so by default warm up by time
-    if args.warmup is None:
-        n_warm, t_w = 0, time.perf_counter()
-        while n_warm < 10 or time.perf_counter() - t_w < WARMUP_S:
-            for _ in range(10):
-                step()
-            n_warm += 10
-            torch.cuda.synchronize()
-        args.warmup = n_warm
-    else:
-        for _ in range(args.warmup):
-            step()
+    # ~15% slower than steady state)
+    n_warm, t_w = 0, time.perf_counter()
+    for _ in range(args.warmup):
+        step()
+        n_warm += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - t_w < WARMUP_S:
+        for _ in range(10):
+            step()
+        n_warm += 10
+        torch.cuda.synchronize()
+    warmup_s = time.perf_counter() - t_w
 
     # timed region: K steps back to back, wall clock for the job throughput and
     # one pair of HIP events on the launch stream for the average launch time
@@ -402,6 +445,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     gpu_ms = e0.elapsed_time(e1)
+
+    # the outputs of the last timed step (every call writes its own buffer)
+    outs = [c.out.clone() for c in calls]
+    # determinism (not timed): five more steps give the same bits
+    identical = True
+    for _ in range(5):
+        step()
+        identical &= all(bool(torch.equal(c.out, o)) for c, o in zip(calls, outs))
+    torch.cuda.synchronize()
 
     # diagnostics (not timed): HIP events around every call of a few steps
     n_diag = min(args.steps, 10)
@@ -438,6 +490,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_s": round(warmup_s, 3),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -465,8 +519,13 @@ def main():
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:
         result["config"]["page_size"] = wl.page_size
+    result["determinism"] = {"runs": 6, "identical": identical,
+                             "of": "the outputs of the last timed step and of five more steps, bit for bit"}
+    result["parity"] = None
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.cpu_threads)
+        gpu_out = [o.float().cpu().numpy().reshape(T, H, D) for o, (T, _) in zip(outs, wl.chunks)]
+        result["cpu_baseline"], result["parity"] = cpu_baseline(wl, x, args.cpu_seconds,
+                                                                args.cpu_threads, gpu_out)
     print(json.dumps(result), flush=True)
 
 

@@ -58,6 +58,7 @@
 #include <algorithm>
 #include <type_traits>
 #include <mutex>
+#include <vector>
 
 #include "prefill_attn.h"
 
@@ -215,6 +216,12 @@ __device__ inline int first_key(int pos, int window) {
 struct Tile {
     int kvh, split, t0, t_last;
     int kt_begin, kt_end;          // this work-group's KV tiles [begin, end)
+    // Keys the work-group's rows read: [klo, kend), from the first row's
+    // window start to the last row's position.  The other rows of its first
+    // and last KV tile are loaded as zeros (their keys are valid for no row
+    // here), so whatever the cache holds there cannot reach the output
+    // through a product with probability 0.
+    int klo, kend;
 };
 
 template <int BK>
@@ -240,34 +247,41 @@ __device__ inline Tile locate(const Params &p) {
     const int per = (ke - kb + p.S - 1) / p.S;
     w.kt_begin = min(ke, kb + w.split * per);
     w.kt_end = min(ke, w.kt_begin + per);
+    w.klo = lo;
+    w.kend = hi + 1;
     return w;
 }
 
-// Paired work-groups (causal, no window, no key split): item -> (kv head, j);
+// Paired work-groups (causal, no window, no key split, an even number of
+// query tiles; the host plans pairs only then): item -> (kv head, j);
 // wavefronts 0..3 take the long query tile nq-1-j, wavefronts 4..7 the short
-// one j (none when they coincide, odd nq).  The short tile's keys are a prefix
-// of the long one's, so the work-group steps through the long tile's KV range
-// and every tile both need comes into LDS once instead of once per
-// work-group; the short tile's wavefronts skip the tiles past their rows.
-// Returns the group's tile; kb/ke get the work-group's KV range.
+// one j.  The short tile's keys are a prefix of the long one's, so the
+// work-group steps through the long tile's KV range and every tile both need
+// comes into LDS once instead of once per work-group; the short tile's
+// wavefronts skip the tiles past their rows.  Returns the group's tile; kb/ke
+// get the work-group's KV range.
 template <int BK>
 __device__ inline Tile locate_pair(const Params &p, int grp, int &kb, int &ke) {
     const int item = xcd_logical_item(blockIdx.x, p.n_items);
-    const int np = (p.nq + 1) / 2;
+    const int np = p.nq / 2;
     const int j = item % np, kvh = item / np;
     const int ql = p.nq - 1 - j, qs = j;
     const int tl0 = ql * p.TQ, tl1 = min(tl0 + p.TQ, p.T) - 1;
     const int ts0 = qs * p.TQ, ts1 = min(ts0 + p.TQ, p.T) - 1;
-    // union of the two KV ranges (the short tile's rows end no later than the long one's)
-    kb = min(first_key(p.start_pos + tl0, p.window), first_key(p.start_pos + ts0, p.window)) / BK;
+    // union of the two key ranges: the short tile's rows start no later and
+    // end no later than the long one's
+    const int klo = first_key(p.start_pos + ts0, p.window);
+    kb = klo / BK;
     ke = (p.start_pos + tl1) / BK + 1;
     Tile t;
     t.kvh = kvh;
     t.split = 0;
     t.t0 = grp == 0 ? tl0 : ts0;
-    t.t_last = grp == 0 ? tl1 : (qs == ql ? -1 : ts1);     // odd nq: the middle tile alone
+    t.t_last = grp == 0 ? tl1 : ts1;
     t.kt_begin = kb;
     t.kt_end = ke;
+    t.klo = klo;
+    t.kend = p.start_pos + tl1 + 1;
     return t;
 }
 
@@ -404,20 +418,21 @@ constexpr int kMaxHeadBytes = 0x7FE00000;
 constexpr int kPastRange = 0x7FF00000;
 
 // Ring cache (sliding-window layers): key j of a kv head sits in slot
-// j % ring.  When the ring is a multiple of the tile and the tile ends before
-// L (ring_tile_linear), the tile's rows sit in consecutive slots from
+// j % ring.  kend is the first key past the work-group's keys (at most L):
+// rows at keys >= kend read as zero, like the rows past L of a linear cache.
+// When the ring is a multiple of the tile and the tile ends before kend
+// (ring_tile_linear), the tile's rows sit in consecutive slots from
 // s0 = j0 % ring: the linear offsets with s0 rows added as the scalar offset.
 // Otherwise ring_offsets: lin[i] is the offset lane load i of the tile would
 // have in a linear cache, row * row_bytes + chunk; each row finds its slot
 // s0 + row, wrapped once past the ring's end (rings of at least BK slots; the
 // wrap test compares lin itself, since chunk < row_bytes) or reduced by
-// division, and rows at keys >= L read as zero, like the rows past L of a
-// linear cache.  s0 is kept by the caller (ring_advance).
-[[maybe_unused]] __device__ inline bool ring_tile_linear(const Params &p, int j0, int BK) {
-    return p.ring % BK == 0 && j0 <= p.L - BK;   // j0 + BK <= L without forming it (may be 2^31)
+// division.  s0 is kept by the caller (ring_advance).
+[[maybe_unused]] __device__ inline bool ring_tile_linear(const Params &p, int j0, int BK, int kend) {
+    return p.ring % BK == 0 && j0 <= kend - BK;   // j0 + BK <= kend without forming it (may be 2^31)
 }
 template <int N>
-__device__ inline void ring_offsets(const Params &p, int j0, int s0, int BK, int row_bytes,
+__device__ inline void ring_offsets(const Params &p, int j0, int s0, int BK, int row_bytes, int kend,
                                     const int (&lin)[N], int (&off)[N]) {
     if (p.ring >= BK) {
         const int wrap_at = (p.ring - s0) * row_bytes, base = s0 * row_bytes;
@@ -431,8 +446,8 @@ __device__ inline void ring_offsets(const Params &p, int j0, int s0, int BK, int
             off[i] = ((s0 + row) % p.ring) * row_bytes + (lin[i] - row * row_bytes);
         }
     }
-    if (j0 > p.L - BK) {
-        const int end = (p.L - j0) * row_bytes;
+    if (j0 > kend - BK) {
+        const int end = (kend - j0) * row_bytes;
 #pragma unroll
         for (int i = 0; i < N; ++i) off[i] = lin[i] >= end ? kPastRange : off[i];
     }
@@ -448,13 +463,14 @@ __device__ inline void ring_offsets(const Params &p, int j0, int s0, int BK, int
 #if defined(__HIP_DEVICE_COMPILE__)
 // Paged cache: the K/V descriptors of the tile whose first key is j0 (a page
 // holds whole tiles), based at kv head kvh's rows of page `page` and covering
-// the page's rows below L, so rows at keys >= L read as zero; an entry outside
-// the pool reads as zeros.  soff = the tile's first row within the page.
-__device__ inline void paged_rsrc(const Params &p, int kvh, int j0, int row_bytes, int page,
+// the page's rows below kend (the first key past the work-group's keys, at
+// most L), so rows at keys >= kend read as zero; an entry outside the pool
+// reads as zeros.  soff = the tile's first row within the page.
+__device__ inline void paged_rsrc(const Params &p, int kvh, int j0, int row_bytes, int page, int kend,
                                   __amdgpu_buffer_rsrc_t &rk, __amdgpu_buffer_rsrc_t &rv, int &soff) {
     const int r0 = j0 & ((1 << p.page_shift) - 1);
     const bool ok = page >= 0 && page < p.num_pages;
-    const int rows = ok ? min(1 << p.page_shift, p.L - (j0 - r0)) : 0;
+    const int rows = ok ? min(1 << p.page_shift, kend - (j0 - r0)) : 0;
     const int64_t base = ok ? ((((int64_t)page * p.KVH + kvh) << p.page_shift) * row_bytes) : 0;
     rk = head_rsrc((const uint8_t *)p.k + base, rows * row_bytes);
     rv = head_rsrc((const uint8_t *)p.v + base, rows * row_bytes);
@@ -567,7 +583,8 @@ struct Ones {
 // consumed: for each KV tile, each 16-byte chunk c = (block * steps + step) *
 // 64 + lane holds the 8 values that lane feeds to one MFMA, so the attention
 // kernels copy tiles into LDS verbatim and read each operand with one
-// contiguous ds_read_b128.  Keys at or past L are written as zeros.
+// contiguous ds_read_b128.  Keys no row of the call reads (at or past L,
+// below the first query's window) are written as zeros.
 //   M32 (32x32x16 MFMA): block = 32-wide d block, step = 16 keys; lane
 //        (l%32, l/32), element e: key 16*step + 8*(e/4) + 4*(l/32) + e%4,
 //        d = 32*block + l%32
@@ -578,6 +595,7 @@ template <int D, int BK, bool M16>
 __global__ __launch_bounds__(256) void pack_v_operands(Params p, uint16_t *vop) {
     const uint16_t *v = (const uint16_t *)p.v;
     const int L = p.L, kt_lo = p.vop_kt_lo, ntiles = p.vop_tiles;
+    const int jlo = first_key(p.start_pos, p.window);   // no row of the call reads keys below
     constexpr int PITCH = D + 2;               // LDS row pitch (elements): column reads spread banks
     constexpr int CHUNKS = BK * D / 8;
     __shared__ uint32_t t32[BK * PITCH / 2];
@@ -587,7 +605,7 @@ __global__ __launch_bounds__(256) void pack_v_operands(Params p, uint16_t *vop) 
     for (int cidx = threadIdx.x; cidx < CHUNKS; cidx += 256) {
         const int key = cidx / (D / 8), c8 = cidx % (D / 8);
         const int j = j0 + key;
-        const int64_t src = j < L ? kv_row<D>(p, kvh, j) : -1;   // any cache layout
+        const int64_t src = j >= jlo && j < L ? kv_row<D>(p, kvh, j) : -1;   // any cache layout
         const u32x4 val = src >= 0 ? *(const u32x4 *)(v + src + 8 * c8) : u32x4{0, 0, 0, 0};
         uint32_t *row = t32 + (key * PITCH + 8 * c8) / 2;
         row[0] = val[0];
@@ -653,10 +671,13 @@ void attn_fwd16(Params p) {
         ke_all = w.kt_end;
     }
     const Rows r = rows_of(p, w, (NW == 8 && p.pair) ? (wave & 3) : wave, l32);
+    // a linear cache's descriptors end at the work-group's last key (rows past
+    // it read as zero); a ring's cover its slots (ring_offsets cuts them)
+    const int kv_range = LAYOUT == kLinear ? w.kend * ROW_BYTES : p.kv_bytes;
     const __amdgpu_buffer_rsrc_t rk =
-        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, kv_range);
     const __amdgpu_buffer_rsrc_t rv =
-        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+        head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, kv_range);
 
     // DMA source offsets (bytes, relative to the tile's first row) of this lane
     int koff[LOADS], voff[LOADS];
@@ -696,7 +717,9 @@ void attn_fwd16(Params p) {
     }
 
     u32x4 qreg[D / 16];
-    {
+    // Q rows, loaded after the first K/V tile's DMA has been issued so that
+    // the two HBM round trips overlap
+    auto load_q = [&]() {
         const uint16_t *qp = (const uint16_t *)p.q + (int64_t)(r.ok ? r.t : 0) * p.q_row_stride +
                              (int64_t)r.h * D + 8 * g;
 #pragma unroll
@@ -708,7 +731,7 @@ void attn_fwd16(Params p) {
         for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
             for (int e = 0; e < 4; ++e) qreg[ks][e] = Ty::scale2(qreg[ks][e], p.c);
-    }
+    };
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -724,37 +747,74 @@ void attn_fwd16(Params p) {
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
     int ring_s = 0;     // ring caches: slot of the next tile's first key
-    auto issue = [&](int kt, int kdst, int vdst) {
+    // Issue the DMA of KV tile kt into the K and V buffers at kdst / vdst.
+    // FIRST (the work-group's first tile): rows below w.klo get an offset
+    // past the descriptor's range, so they arrive as zeros.
+    auto issue = [&](int kt, int kdst, int vdst, auto FIRST_) {
+        constexpr bool FIRST = decltype(FIRST_)::value;
         // LDS destination (M0) of this wave's chunks: one scalar base, made
         // opaque at every issue so that the compiler derives the per-chunk
         // values here instead of keeping all sixteen live through the loop
         uint32_t mb = (uint32_t)(uintptr_t)LDS_PTR(smem) + wave * LOADS * 1024;
         asm volatile("" : "+s"(mb));
+        // per-lane offsets with the tile's scalar base folded in, rows below
+        // klo cut off (first tile only)
+        auto cut = [&](const int (&in)[LOADS], int (&o)[LOADS], int base) {
+            const int lim = (w.klo - kt * BK) * ROW_BYTES;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) o[i] = in[i] < lim ? kPastRange : in[i] + base;
+        };
         if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
+            if constexpr (FIRST) {
+                int ko[LOADS], vo[LOADS];
+                cut(koff, ko, base);
+                cut(voff, vo, base);
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], base, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], base, 0, 0);
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_ADDR(mb + kdst + i * 1024), 16, ko[i], 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_ADDR(mb + vdst + i * 1024), 16, vo[i], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], base, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], base, 0, 0);
+                }
             }
         } else if constexpr (LAYOUT == kPaged) {
             __amdgpu_buffer_rsrc_t pk, pv;
             int soff;
-            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, pk, pv, soff);
+            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, w.kend, pk, pv, soff);
+            if constexpr (FIRST) {
+                int ko[LOADS], vo[LOADS];
+                cut(koff, ko, soff);
+                cut(voff, vo, soff);
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], soff, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], soff, 0, 0);
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        pk, LDS_ADDR(mb + kdst + i * 1024), 16, ko[i], 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        pv, LDS_ADDR(mb + vdst + i * 1024), 16, vo[i], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        pk, LDS_ADDR(mb + kdst + i * 1024), 16, koff[i], soff, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        pv, LDS_ADDR(mb + vdst + i * 1024), 16, voff[i], soff, 0, 0);
+                }
             }
             pg_next = page_of(p, (int64_t)(kt + 1) * BK);     // one tile ahead of its use
         } else {
             const int s0 = ring_s, j0 = kt * BK;
             ring_s = ring_advance(ring_s, BK, p.ring);
-            if (ring_tile_linear(p, j0, BK)) {
+            if (!FIRST && ring_tile_linear(p, j0, BK, w.kend)) {
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -764,8 +824,16 @@ void attn_fwd16(Params p) {
                 }
             } else {
                 int ko[LOADS], vo[LOADS];
-                ring_offsets(p, j0, s0, BK, D * 2, koff, ko);
-                ring_offsets(p, j0, s0, BK, D * 2, voff, vo);
+                ring_offsets(p, j0, s0, BK, D * 2, w.kend, koff, ko);
+                ring_offsets(p, j0, s0, BK, D * 2, w.kend, voff, vo);
+                if constexpr (FIRST) {
+                    const int lim = (w.klo - j0) * ROW_BYTES;
+#pragma unroll
+                    for (int i = 0; i < LOADS; ++i) {
+                        ko[i] = koff[i] < lim ? kPastRange : ko[i];
+                        vo[i] = voff[i] < lim ? kPastRange : vo[i];
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -884,21 +952,24 @@ void attn_fwd16(Params p) {
     using B1K = std::integral_constant<int, TILE_BYTES>;
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
+    using First = std::true_type;
+    using Next = std::false_type;
     if (kb0 < ke) {
         if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
         if constexpr (LAYOUT == kRing) ring_s = kb0 * BK % p.ring;
-        issue(kb0, B0K::value, B0V::value);
+        issue(kb0, B0K::value, B0V::value, First{});
+        load_q();
         wait_vmem();
         __syncthreads();
         for (int kt = kb0; kt < ke; kt += 2) {
             // tile kt in buffer 0 while tile kt+1 streams into buffer 1
-            if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
+            if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value, Next{});
             tile(B0K{}, B0V{}, kt);
             wait_vmem();
             __syncthreads();
             if (kt + 1 >= ke) break;
             // tile kt+1 in buffer 1 while tile kt+2 streams into buffer 0
-            if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
+            if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value, Next{});
             tile(B1K{}, B1V{}, kt + 1);
             wait_vmem();
             __syncthreads();
@@ -989,11 +1060,15 @@ void attn_fwd16_r16(Params p) {
     const int l16 = lane & 15, g4 = lane >> 4;
     const Tile w = locate<BK>(p);
     const Rows r = rows_of<kRowsPerWave16>(p, w, hw, l16);
+    // a linear cache's descriptors end at the work-group's last key (rows past
+    // it read as zero); a ring's cover its slots (ring_offsets cuts them); the
+    // operand-order V copy holds zeros at keys no row of the call reads
+    const int kv_range = LAYOUT == kLinear ? w.kend * ROW_BYTES : p.kv_bytes;
     const __amdgpu_buffer_rsrc_t rk =
-        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+        head_rsrc((const uint16_t *)p.k + (int64_t)w.kvh * p.kv_head_stride, kv_range);
     const __amdgpu_buffer_rsrc_t rv =
         VPACK ? head_rsrc(p.vop + (int64_t)w.kvh * p.vop_tiles * (BK * D), p.vop_tiles * TILE_BYTES)
-              : head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, p.kv_bytes);
+              : head_rsrc((const uint16_t *)p.v + (int64_t)w.kvh * p.kv_head_stride, kv_range);
 
     int koff[LOADS], voff[LOADS];
 #pragma unroll
@@ -1036,7 +1111,9 @@ void attn_fwd16_r16(Params p) {
     }
 
     u32x4 qreg[NKS];
-    {
+    // Q rows, loaded after the first K/V tile's DMA has been issued so that
+    // the two HBM round trips overlap
+    auto load_q = [&]() {
         const uint16_t *qp = (const uint16_t *)p.q + (int64_t)(r.ok ? r.t : 0) * p.q_row_stride +
                              (int64_t)r.h * D + 8 * g4;
 #pragma unroll
@@ -1050,7 +1127,7 @@ void attn_fwd16_r16(Params p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qreg[ks][e] = Ty::scale2(qreg[ks][e], p.c);
         }
-    }
+    };
 
     f32x4v o[NDB];
 #pragma unroll
@@ -1066,33 +1143,59 @@ void attn_fwd16_r16(Params p) {
 
     int pg_next = -1;   // paged caches: page of the next tile this wave issues
     int ring_s = 0;     // ring caches: slot of the next tile's first key
-    auto issue = [&](int kt, int kdst, int vdst) {
+    // Issue the DMA of KV tile kt into the K and V buffers at kdst / vdst.
+    // FIRST (a key half's first tile): rows below w.klo get an offset past the
+    // descriptor's range, so they arrive as zeros (the operand-order V copy
+    // already holds zeros there).
+    auto issue = [&](int kt, int kdst, int vdst, auto FIRST_) {
+        constexpr bool FIRST = decltype(FIRST_)::value;
+        // per-lane offsets with the tile's scalar base folded in, rows below
+        // klo cut off (first tile only)
+        auto cut = [&](const int (&in)[LOADS], int (&o)[LOADS], int base) {
+            const int lim = (w.klo - kt * BK) * ROW_BYTES;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) o[i] = in[i] < lim ? kPastRange : in[i] + base;
+        };
         if constexpr (LAYOUT == kLinear) {
             const int base = kt * BK * D * 2;
             const int vbase_t = VPACK ? (kt - p.vop_kt_lo) * TILE_BYTES : base;
+            int ko[LOADS], vo[LOADS];
+            if constexpr (FIRST) {
+                cut(koff, ko, base);
+                if constexpr (!VPACK) cut(voff, vo, base);
+            }
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], base, 0, 0);
+                    rk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, FIRST ? ko[i] : koff[i],
+                    FIRST ? 0 : base, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], vbase_t, 0, 0);
+                    rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16,
+                    FIRST && !VPACK ? vo[i] : voff[i], FIRST && !VPACK ? 0 : vbase_t, 0, 0);
             }
         } else if constexpr (LAYOUT == kPaged) {
             // the operand-ordered V copy is linear in the call's tiles
             __amdgpu_buffer_rsrc_t pk, pv;
             int soff;
-            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, pk, pv, soff);
+            paged_rsrc(p, w.kvh, kt * BK, D * 2, pg_next, w.kend, pk, pv, soff);
+            int ko[LOADS], vo[LOADS];
+            if constexpr (FIRST) {
+                cut(koff, ko, soff);
+                if constexpr (!VPACK) cut(voff, vo, soff);
+            }
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    pk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, koff[i], soff, 0, 0);
+                    pk, LDS_PTR(sm + kdst + (hw * LOADS + i) * 1024), 16, FIRST ? ko[i] : koff[i],
+                    FIRST ? 0 : soff, 0, 0);
                 if constexpr (VPACK)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         rv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i],
                         (kt - p.vop_kt_lo) * TILE_BYTES, 0, 0);
                 else
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        pv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, voff[i], soff, 0, 0);
+                        pv, LDS_PTR(sm + vdst + (hw * LOADS + i) * 1024), 16, FIRST ? vo[i] : voff[i],
+                        FIRST ? 0 : soff, 0, 0);
             }
             pg_next = page_of(p, (int64_t)(kt + 1) * BK);     // one tile ahead of its use
         } else {
@@ -1101,7 +1204,7 @@ void attn_fwd16_r16(Params p) {
             const int s0 = ring_s, j0 = kt * BK;
             ring_s = ring_advance(ring_s, BK, p.ring);
             const int vpack_base = (kt - p.vop_kt_lo) * TILE_BYTES;
-            if (ring_tile_linear(p, j0, BK)) {
+            if (!FIRST && ring_tile_linear(p, j0, BK, w.kend)) {
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1112,8 +1215,16 @@ void attn_fwd16_r16(Params p) {
                 }
             } else {
                 int ko[LOADS], vo[LOADS];
-                ring_offsets(p, j0, s0, BK, D * 2, koff, ko);
-                if constexpr (!VPACK) ring_offsets(p, j0, s0, BK, D * 2, voff, vo);
+                ring_offsets(p, j0, s0, BK, D * 2, w.kend, koff, ko);
+                if constexpr (!VPACK) ring_offsets(p, j0, s0, BK, D * 2, w.kend, voff, vo);
+                if constexpr (FIRST) {
+                    const int lim = (w.klo - j0) * ROW_BYTES;
+#pragma unroll
+                    for (int i = 0; i < LOADS; ++i) {
+                        ko[i] = koff[i] < lim ? kPastRange : ko[i];
+                        if constexpr (!VPACK) vo[i] = voff[i] < lim ? kPastRange : vo[i];
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -1252,20 +1363,23 @@ void attn_fwd16_r16(Params p) {
     using B0V = std::integral_constant<int, 2 * TILE_BYTES>;
     using B1V = std::integral_constant<int, 3 * TILE_BYTES>;
     const int kb0 = w.kt_begin, ke = w.kt_end;
+    using First = std::true_type;
+    using Next = std::false_type;
     if constexpr (KSPLIT == 1) {
         if (kb0 < ke) {
             if constexpr (LAYOUT == kPaged) pg_next = page_of(p, kb0 * BK);
             if constexpr (LAYOUT == kRing) ring_s = kb0 * BK % p.ring;
-            issue(kb0, B0K::value, B0V::value);
+            issue(kb0, B0K::value, B0V::value, First{});
+            load_q();
             wait_vmem();
             __syncthreads();
             for (int kt = kb0; kt < ke; kt += 2) {
-                if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value);
+                if (kt + 1 < ke) issue(kt + 1, B1K::value, B1V::value, Next{});
                 tile(B0K{}, B0V{}, kt);
                 wait_vmem();
                 __syncthreads();
                 if (kt + 1 >= ke) break;
-                if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value);
+                if (kt + 2 < ke) issue(kt + 2, B0K::value, B0V::value, Next{});
                 tile(B1K{}, B1V{}, kt + 1);
                 wait_vmem();
                 __syncthreads();
@@ -1281,17 +1395,18 @@ void attn_fwd16_r16(Params p) {
         if (niter > 0) {
             if constexpr (LAYOUT == kPaged) pg_next = hb < he ? page_of(p, hb * BK) : -1;
             if constexpr (LAYOUT == kRing) ring_s = hb * BK % p.ring;
-            if (hb < he) issue(hb, B0K::value, B0V::value);
+            if (hb < he) issue(hb, B0K::value, B0V::value, First{});
+            load_q();
             wait_vmem();
             __syncthreads();
             for (int it = 0; it < niter; it += 2) {
                 const int kt = hb + it;
-                if (kt + 1 < he) issue(kt + 1, B1K::value, B1V::value);
+                if (kt + 1 < he) issue(kt + 1, B1K::value, B1V::value, Next{});
                 if (kt < he) tile(B0K{}, B0V{}, kt);
                 wait_vmem();
                 __syncthreads();
                 if (it + 1 >= niter) break;
-                if (kt + 2 < he) issue(kt + 2, B0K::value, B0V::value);
+                if (kt + 2 < he) issue(kt + 2, B0K::value, B0V::value, Next{});
                 if (kt + 1 < he) tile(B1K{}, B1V{}, kt + 1);
                 wait_vmem();
                 __syncthreads();
@@ -1383,7 +1498,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
     const int l32 = lane & 31, g = lane >> 5;
     const Tile w = locate<BK>(p);
     const Rows r = rows_of(p, w, wave, l32);
-    const int L = p.start_pos + p.T;
 
     float qreg[HALF];
     {
@@ -1412,8 +1526,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * kThreads;
             const int key = idx / (D / 4), c4 = idx % (D / 4);
+            // keys the work-group's rows read, any cache layout; the rest load as zeros
             const int j = j0 + key;
-            const int64_t row = j < L ? kv_row<D>(p, w.kvh, j) : -1;   // any cache layout
+            const int64_t row = j >= w.klo && j < w.kend ? kv_row<D>(p, w.kvh, j) : -1;
             kbuf[i] = row >= 0 ? *(const f32x4 *)((const float *)p.k + row + 4 * c4)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -1425,7 +1540,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(Params p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + 4 * kq + u;
-                const int64_t row = j < L ? kv_row<D>(p, w.kvh, j) : -1;
+                const int64_t row = j >= w.klo && j < w.kend ? kv_row<D>(p, w.kvh, j) : -1;
                 vbuf[i][u] = row >= 0 ? *(const f32x4 *)((const float *)p.v + row + 4 * c4)
                                       : f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -1824,20 +1939,21 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     pl->TQ = var->rows / pl->G;
     pl->nq = (int)cdiv(T, pl->TQ);
     pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq);
-    // Causal tiles without a window and without key splits, on a grid that
-    // fills every resident slot and whose pairs fit one per CU: the long and
-    // the short query tile of a kv head go into one work-group whose
-    // wavefront groups share the KV tiles of the common key prefix (same rows
-    // per group, so the tile size and the plan above stay valid).  On a
-    // smaller grid the pair would only slow the long tile down; on a larger
-    // one (a second round of work-groups) the fixed pairs lose to the
-    // dispatcher refilling CUs as single tiles finish.
-    if (pl->S == 1 && pl->nq >= 2 && (int64_t)pl->nq * KVH >= (int64_t)kCus * var->groups_per_cu &&
-        (int64_t)((pl->nq + 1) / 2) * KVH <= (int64_t)kCus &&
-        (window == 0 || (int64_t)window >= (int64_t)start_pos + T))
+    // Causal tiles without a window and without key splits whose grid is
+    // exactly one round of two work-groups per CU (nq * KVH = 512 with nq
+    // even; at head_dim 128 with 16-bit inputs that is the 2048-token chunk of
+    // 32 query heads over 8 kv heads): the long and the short query tile of a
+    // kv head go into one work-group whose wavefront groups share the KV
+    // tiles of the common key prefix (same rows per group, so the tile size
+    // and the plan above stay valid), one such pair per CU.  On a smaller
+    // grid the pair would only slow the long tile down; on a larger one (a
+    // second round of work-groups) the fixed pairs lose to the dispatcher
+    // refilling CUs as single tiles finish (measured on the 8192-token call).
+    if (pl->S == 1 && pl->nq % 2 == 0 && (int64_t)pl->nq * KVH == 2 * (int64_t)kCus &&
+        var->groups_per_cu == 2 && (window == 0 || (int64_t)window >= (int64_t)start_pos + T))
         if (const Variant *alt = find_ksplit_variant(dtype, D, 3))
             if (alt->rows == var->rows) var = pl->var = alt;
-    const int64_t items = var->ksplit == 3 ? (int64_t)((pl->nq + 1) / 2) * KVH
+    const int64_t items = var->ksplit == 3 ? (int64_t)(pl->nq / 2) * KVH
                                            : (int64_t)pl->nq * KVH * pl->S;
     if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
     pl->items = (int)items;
@@ -1970,37 +2086,49 @@ int check_args(int dtype, const void *q, int64_t q_row_stride, const void *k, co
     return PA_OK;
 }
 
-// Per-device scratch for the packed entry points.
-struct DeviceScratch {
-    void *ptr = nullptr;
-    size_t bytes = 0;
+// Scratch of the packed entry points: one buffer per (device, stream), so
+// that calls on different streams never share one, grown on demand.  The
+// lock is held from the lookup through the launch: a call that grows a
+// buffer first waits for the work already enqueued on its stream (the only
+// work that can use it) and no other thread can hold the old pointer.
+struct StreamScratch {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
 };
 std::mutex g_scratch_mutex;
-DeviceScratch g_scratch[64];
+std::vector<StreamScratch> g_scratch;
 
-int scratch_for(size_t need, void **out) {
+// Called with g_scratch_mutex held.
+int scratch_for(size_t need, hipStream_t stream, void **out) {
     *out = nullptr;
     if (need == 0) return PA_OK;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PA_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_scratch_mutex);
-    DeviceScratch &s = g_scratch[dev];
-    if (s.bytes < need) {
-        if (s.ptr) {
-            // work already enqueued may still read the old buffer
-            if (hipDeviceSynchronize() != hipSuccess) return PA_ERR_HIP;
-            if (hipFree(s.ptr) != hipSuccess) return PA_ERR_HIP;
-            s.ptr = nullptr;
-            s.bytes = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    StreamScratch *s = nullptr;
+    for (StreamScratch &e : g_scratch)
+        if (e.dev == dev && e.stream == stream) s = &e;
+    if (!s) {
+        g_scratch.push_back(StreamScratch{dev, stream, nullptr, 0});
+        s = &g_scratch.back();
+    }
+    if (s->bytes < need) {
+        if (s->ptr) {
+            // work already enqueued on this stream may still read the old buffer
+            if (hipStreamSynchronize(stream) != hipSuccess) return PA_ERR_HIP;
+            if (hipFree(s->ptr) != hipSuccess) return PA_ERR_HIP;
+            s->ptr = nullptr;
+            s->bytes = 0;
         }
         const size_t grow = need + need / 4;
-        if (hipMalloc(&s.ptr, grow) != hipSuccess) {
-            s.ptr = nullptr;
+        if (hipMalloc(&s->ptr, grow) != hipSuccess) {
+            s->ptr = nullptr;
             return PA_ERR_HIP;
         }
-        s.bytes = grow;
+        s->bytes = grow;
     }
-    *out = s.ptr;
+    *out = s->ptr;
     return PA_OK;
 }
 
@@ -2014,12 +2142,12 @@ int run_packed(int dtype, const void *q, const void *k, const void *v, float *ou
     Plan pl;
     st = make_plan(dtype, T, start_pos, H, KVH, D, window, &pl);
     if (st != PA_OK) return st;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
     void *ws = nullptr;
-    st = scratch_for(pl.ws_bytes, &ws);
+    st = scratch_for(pl.ws_bytes, (hipStream_t)stream, &ws);
     if (st != PA_OK) return st;
     return launch(pl, dtype, q, row, k, v, kvs, CacheLayout{}, out, row, PA_DTYPE_F32, T, start_pos,
-                  H, KVH, D,
-                  window, ws, (hipStream_t)stream);
+                  H, KVH, D, window, ws, (hipStream_t)stream);
 }
 
 // Plan, workspace check and launch of the strided entry points (arguments checked).

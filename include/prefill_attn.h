@@ -17,10 +17,13 @@
  *   softmax of the valid scores weights the value rows:
  *       out_t = sum_j softmax(s)_j * v_j                      (Step 3)
  *   Masked keys contribute exactly nothing.  window <= 0 means no window.
- *   (Keys are loaded in tiles of 32 or 64 positions: the cache rows of keys
- *   [0, L) that share a tile with a row's band are read and weighted by 0,
- *   so they must hold finite values, as every written cache does; tiles
- *   outside every row's band and rows past L are never read.)
+ *   Keys that no row of the call reads (below the first query's window
+ *   start, and at or past L) never reach out: the kernels skip them or load
+ *   them as zeros, so those cache rows may hold anything, NaN included.  A
+ *   non-finite value at a key that some row reads makes that row's output
+ *   non-finite, as the definition does; since the query rows of one kv head
+ *   that are computed together (up to 128 (token, head) rows) share each K/V
+ *   tile, it can also reach the other rows of that group.
  *
  * Layouts (all element offsets, row-major; same page, "Layout"):
  *   q        (t, h, d)  at q[t*q_row_stride + h*head_dim + d]
@@ -91,12 +94,14 @@ extern "C" {
 /*
  * Packed entry points: q [T][num_heads][head_dim], caches
  * [num_kv_heads][L][head_dim] with L = start_pos + T, out [T][num_heads][head_dim].
- * Scratch memory (bf16/fp16 inputs: a copy of the call's V rows rearranged
- * into matrix-core operand order; every dtype: split-KV partial results when
- * the keys are split) comes from a per-device buffer the library allocates on
- * first need and grows (hipMalloc; growing synchronises the device once).
- * Calls that run concurrently on one device share that buffer and must be
- * ordered on one stream.
+ * Scratch memory (bf16/fp16 inputs at head_dim 512: a copy of the call's V
+ * rows rearranged into matrix-core operand order; every dtype: split-KV
+ * partial results when the keys are split) comes from a buffer per (device,
+ * stream) that the library allocates on first need and grows (hipMalloc;
+ * growing first waits for the work already enqueued on that stream, the only
+ * work that can use the old buffer).  Calls from several host threads are
+ * safe (a lock covers the lookup and the launch), and calls on different
+ * streams never share a buffer.  Buffers live until the process ends.
  */
 int prefill_attn_f32(const float *q, const float *k_cache, const float *v_cache, float *out,
                      int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,

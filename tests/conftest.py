@@ -19,3 +19,13 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.default()
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Worst GPU-vs-oracle errors per case family and dtype (GPU runs only)."""
+    mod = sys.modules.get("gpu_util")
+    if mod is None or not getattr(mod, "RECORD", None):
+        return
+    terminalreporter.write_sep("=", "parity: worst |gpu - oracle| per case family and dtype")
+    for line in mod.summary_lines():
+        terminalreporter.write_line(line)

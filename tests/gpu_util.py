@@ -34,14 +34,45 @@ def errors(gpu: np.ndarray, ref: np.ndarray):
     return max_abs, rel
 
 
-def assert_parity(gpu, ref, dtype, what=""):
+# every comparison made in this process: (group, dtype, what, rows, max_abs, rel_rms);
+# the test session prints the worst per group and dtype at its end
+RECORD = []
+
+
+def assert_parity(gpu, ref, dtype, what="", group=None, record=True):
+    """Fail unless gpu (any shape, last axis head_dim) meets both bars against
+    the oracle's ref.  group names the case family in the end-of-session
+    summary (default: the first word of what)."""
+    gpu = np.asarray(gpu)
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     max_abs, rel = errors(gpu, ref)
+    rows = int(np.prod(gpu.shape[:-1])) if gpu.ndim > 1 else 1
+    if record:
+        RECORD.append((group or (what.split() or ["?"])[0], dtype, what, rows, max_abs, rel))
     print(f"  {what}: max|gpu-oracle| {max_abs:.3e} (bar {TOL_MAX_ABS[dtype]:.0e}), "
-          f"rel-RMS {rel:.3e} (bar {TOL_REL_RMS[dtype]:.0e})", flush=True)
+          f"rel-RMS {rel:.3e} (bar {TOL_REL_RMS[dtype]:.0e}) over {rows} rows", flush=True)
     assert max_abs <= TOL_MAX_ABS[dtype], (what, max_abs)
     assert rel <= TOL_REL_RMS[dtype], (what, rel)
     return max_abs, rel
+
+
+def summary_lines():
+    """Worst max-abs and rel-RMS per (group, dtype) over the comparisons made."""
+    worst = {}
+    for group, dtype, what, rows, max_abs, rel in RECORD:
+        w = worst.setdefault((group, dtype), [0, 0, 0.0, "", 0.0, ""])
+        w[0] += 1
+        w[1] += rows
+        if max_abs >= w[2]:
+            w[2], w[3] = max_abs, what
+        if rel >= w[4]:
+            w[4], w[5] = rel, what
+    out = []
+    for (group, dtype), (n, rows, ma, mwhat, rr, rwhat) in sorted(worst.items()):
+        out.append(f"{group:<28} {dtype:<5} {n:4d} cmp {rows:9d} rows  max-abs {ma:.3e} "
+                   f"(bar {TOL_MAX_ABS[dtype]:.0e})  rel-RMS {rr:.3e} (bar {TOL_REL_RMS[dtype]:.0e})"
+                   f"  worst: {mwhat}")
+    return out
 
 
 def run_packed(x, T, sp, H, KVH, D, W, q_rows=None):
