@@ -53,6 +53,8 @@ def load():
         fn.restype = I
     lib.prefill_attn_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, I, P, SZ, P]
     lib.prefill_attn_ex.restype = I
+    lib.prefill_attn_noalloc_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, I, P]
+    lib.prefill_attn_noalloc_ex.restype = I
     lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, I, P, SZ,
                                          P]
     lib.prefill_attn_ring_ex.restype = I
@@ -79,6 +81,14 @@ def header_functions() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(prefill_\w+)\s*\(", text)))
+
+
+def header_define(name: str) -> int:
+    """Integer value of a #define in include/prefill_attn.h."""
+    m = re.search(r"#define\s+" + re.escape(name) + r"\s+(\d+)", open(HEADER).read())
+    if not m:
+        raise KeyError(name)
+    return int(m.group(1))
 
 
 def strerror(status: int) -> str:
@@ -234,6 +244,28 @@ def prefill_attn_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_
     float32, bfloat16 or float16."""
     return PreparedCall(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                         start_pos, num_heads, num_kv_heads, head_dim, window, workspace, stream)()
+
+
+def prefill_attn_noalloc_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride,
+                            T, start_pos, num_heads, num_kv_heads, head_dim, window=0, stream=None):
+    """prefill_attn_ex without a workspace: the library's fixed per-GPU scratch
+    array serves instead, and nothing is allocated.  Calls that overlap in
+    time on one GPU must not be issued (they share the array)."""
+    dt = _dtype_of(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one storage type")
+    L = start_pos + T
+    _need(q, (T - 1) * q_row_stride + num_heads * head_dim, "q")
+    _need(k_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "k_cache")
+    _need(v_cache, (num_kv_heads - 1) * kv_head_stride + L * head_dim, "v_cache")
+    _need(out, (T - 1) * out_row_stride + num_heads * head_dim, "out")
+    st = load().prefill_attn_noalloc_ex(DTYPE_CODES[dt], q.data_ptr(), q_row_stride, k_cache.data_ptr(),
+                                        v_cache.data_ptr(), kv_head_stride, out.data_ptr(), out_row_stride,
+                                        DTYPE_CODES[_dtype_of(out)], T, start_pos, num_heads, num_kv_heads,
+                                        head_dim, window, _stream(stream))
+    if st != PA_OK:
+        raise PrefillAttnError(st, "prefill_attn_noalloc_ex")
+    return out
 
 
 def prefill_attn_ring_ex(q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_slots, out,

@@ -1881,7 +1881,7 @@ int check_shape(int dtype, int T, int start_pos, int H, int KVH, int D, int wind
 // resident work-group slots finishes first, charging each extra split the
 // cost of writing and merging its partial rows.
 int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int window,
-                  int G, int TQ, int nq) {
+                  int G, int TQ, int nq, int max_splits = kMaxSplits) {
     // a split's partial rows (written, then merged) cost about half a KV tile's
     // work when the query tile is full, proportionally less for short chunks
     const int rows = std::min(T, TQ) * G;
@@ -1898,7 +1898,7 @@ int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int 
     }
     int best = 1;
     double best_cost = 1e300;
-    for (int S = 1; S <= kMaxSplits; ++S) {
+    for (int S = 1; S <= max_splits; ++S) {
         if (S > 1 && cdiv(max_tiles, S) < 4) break;
         const int64_t items = base * S;
         const double waves = (double)cdiv(items, slots);
@@ -1916,7 +1916,7 @@ int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int 
 }
 
 int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window, Plan *pl,
-              bool no_pack = false) {
+              bool no_pack = false, int max_splits = kMaxSplits) {
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st != PA_OK) return st;
     const Variant *var = find_variant(dtype, D);
@@ -1938,7 +1938,7 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     pl->G = H / KVH;
     pl->TQ = var->rows / pl->G;
     pl->nq = (int)cdiv(T, pl->TQ);
-    pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq);
+    pl->S = choose_splits(*var, T, start_pos, H, KVH, window, pl->G, pl->TQ, pl->nq, max_splits);
     // Causal tiles without a window and without key splits whose grid is
     // exactly one round of two work-groups per CU (nq * KVH = 512 with nq
     // even; at head_dim 128 with 16-bit inputs that is the 2048-token chunk of
@@ -2168,6 +2168,42 @@ int run_ex(int dtype, const void *q, int64_t q_row_stride, const void *k, const 
 
 }  // namespace
 
+// ---- scratch without allocation ------------------------------------------------------
+//
+// prefill_attn_noalloc_ex keeps its workspace (split partials, the V copy) in
+// this array instead of memory the library allocates or the caller passes:
+// each GPU the library runs on holds one copy of it until the process ends.
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device on
+// the entry point's first call there (with that device current).  Nothing in
+// it has to start at zero: every byte a call reads was written earlier in the
+// same call.
+
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mutex;
+void *g_noalloc_ptr[kMaxDevices];
+
+// This device's copy of `scratch` (device address), or PA_ERR_HIP.
+int noalloc_scratch(void **out) {
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    if (!g_noalloc_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+        g_noalloc_ptr[dev] = ptr;
+    }
+    *out = g_noalloc_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
 // ---- C ABI -----------------------------------------------------------------------------
 
 extern "C" {
@@ -2205,6 +2241,37 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *
     return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
                   out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
+}
+
+int prefill_attn_noalloc_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_cache,
+                            const void *v_cache, int64_t kv_head_stride, void *out,
+                            int64_t out_row_stride, int out_dtype, int T, int start_pos,
+                            int num_heads, int num_kv_heads, int head_dim, int window, void *stream) {
+    int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride,
+                        (int64_t)start_pos + T, out, out_row_stride, out_dtype, T, start_pos, num_heads,
+                        num_kv_heads, head_dim, window);
+    if (st != PA_OK) return st;
+    // prefill_attn_ex's plan when its workspace fits the array; otherwise V
+    // read in place and the fewest fewer key splits whose partials fit (one
+    // split needs none)
+    Plan pl;
+    st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl);
+    if (st == PA_OK && pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) {
+        st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl, true);
+        while (st == PA_OK && pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES && pl.S > 1)
+            st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, &pl, true,
+                           pl.S - 1);
+    }
+    if (st != PA_OK) return st;
+    if (pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (pl.ws_bytes > 0) {
+        st = noalloc_scratch(&ws);
+        if (st != PA_OK) return st;
+    }
+    return launch(pl, dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
+                  out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window,
+                  ws, (hipStream_t)stream);
 }
 
 int prefill_attn_ring_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_ring,

@@ -131,6 +131,30 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride,
                     int window, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * prefill_attn_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc)
+ * and have no workspace to pass: the same arguments without the workspace.
+ * Its scratch is a fixed array of PA_NOALLOC_SCRATCH_BYTES in device memory,
+ * one per GPU, held from the library's first use on that GPU until the
+ * process ends; nothing is allocated or freed by the call.  When the plan
+ * prefill_attn_ex would use fits in it, that plan runs (same kernels, same
+ * result bits); otherwise V is read in place and the keys are split fewer
+ * times, down to a plan that needs no scratch, so no size is refused for the
+ * scratch's sake (PA_ERR_WORKSPACE would mean it could not fit, which no
+ * plan reaches).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or different threads
+ * without ordering) race on it and must not be issued; calls ordered on one
+ * stream are fine.  Errors as for prefill_attn_ex, plus PA_ERR_HIP when the
+ * array's device address cannot be obtained.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES 33554432   /* 32 MiB */
+int prefill_attn_noalloc_ex(int dtype, const void *q, int64_t q_row_stride,
+                            const void *k_cache, const void *v_cache, int64_t kv_head_stride,
+                            void *out, int64_t out_row_stride, int out_dtype,
+                            int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                            int window, void *stream);
+
+/*
  * Ring cache form (sliding-window layers).  The TensorSharp page "Design:
  * closing the Gemma-4 long-prompt prefill gap", section 4, requirement R4,
  * has sliding-window layers write the K/V of position pos into slot

@@ -20,7 +20,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
                           "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
                           "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write",
-                          "prefill_attn_paged_ex", "prefill_attn_paged_dev_ex"}
+                          "prefill_attn_paged_ex", "prefill_attn_paged_dev_ex", "prefill_attn_noalloc_ex"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -266,3 +266,23 @@ def test_paged_dev_arguments(lib):
     assert call(maxsp=-1) == E
     assert call(T=0) == E
     assert call(P=48) == U
+
+
+def test_noalloc_arguments(lib):
+    """The no-allocation form checks its arguments like prefill_attn_ex,
+    before it looks up its scratch (so nothing here touches a GPU)."""
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    fn = lib.prefill_attn_noalloc_ex
+
+    def call(q=FAKE, qs=256, k=FAKE, v=FAKE, kvs=64 * 64, out=FAKE, os_=256, odt=0, T=4, sp=60, H=4,
+             KVH=2, D=64, W=0, dt=pa.PA_DTYPE_BF16):
+        return fn(dt, q, qs, k, v, kvs, out, os_, odt, T, sp, H, KVH, D, W, None)
+
+    assert call(q=None) == E and call(k=None) == E and call(v=None) == E and call(out=None) == E
+    assert call(T=0) == E and call(sp=-1) == E and call(W=-1) == E and call(H=6, KVH=4) == E
+    assert call(qs=255) == E                 # q row shorter than H * D
+    assert call(kvs=63 * 64) == E            # kv-head stride below L * D
+    assert call(os_=200) == E
+    assert call(D=48) == U and call(dt=7) == U and call(odt=9) == U
+    assert call(q=FAKE + 8) == U             # misaligned
+    assert pa.header_define("PA_NOALLOC_SCRATCH_BYTES") == 32 << 20
