@@ -1416,30 +1416,30 @@ void attn_fwd16_r16(Params p) {
 
     if constexpr (KSPLIT == 2) {
         // the second half hands (O, m, l) of its rows to the wavefront of the
-        // first half that holds the same rows (same hw and lane); the buffers
-        // are free after the loop's last barrier
-        constexpr int NX = NDB * 4 + 2;
-        static_assert(NWH * NX * kWave * 4 <= KSPLIT * 4 * TILE_BYTES, "exchange fits in LDS");
-        float *xch = (float *)smem + hw * NX * kWave + lane;
+        // first half that holds the same rows (same hw and lane), as 16-byte
+        // pieces (lane-consecutive); the buffers are free after the loop's
+        // last barrier
+        constexpr int NX = NDB + 1;
+        static_assert(NWH * NX * kWave * 16 <= KSPLIT * 4 * TILE_BYTES, "exchange fits in LDS");
+        f32x4 *xch = (f32x4 *)smem + hw * NX * kWave + lane;
         if (half == 1) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xch[(4 * db + i) * kWave] = o[db][i];
-            xch[(NX - 2) * kWave] = mref;
-            xch[(NX - 1) * kWave] = lsum;
+            for (int db = 0; db < NDB; ++db) xch[db * kWave] = f32x4{o[db][0], o[db][1], o[db][2], o[db][3]};
+            xch[NDB * kWave] = f32x4{mref, lsum, 0.f, 0.f};
         }
         __syncthreads();
         if (half == 0) {
-            const float m1 = xch[(NX - 2) * kWave], l1 = xch[(NX - 1) * kWave];
-            const float ms = fmaxf(mref, m1);
+            const f32x4 ml = xch[NDB * kWave];
+            const float ms = fmaxf(mref, ml[0]);
             const float a0 = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - ms);
-            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - ms);
+            const float a1 = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - ms);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db) {
+                const f32x4 x = xch[db * kWave];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a0 + xch[(4 * db + i) * kWave] * a1;
-            lsum = lsum * a0 + l1 * a1;
+                for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a0 + x[i] * a1;
+            }
+            lsum = lsum * a0 + ml[1] * a1;
             mref = ms;
         }
     }
