@@ -289,8 +289,8 @@ def kv_write_bench(args):
     torch.cuda.synchronize()
     n_warm, t_w = 0, time.perf_counter()
     with torch.cuda.stream(side):
-        # replays of the K-step graph: at least one, then until WARMUP_S has passed
-        while n_warm < 1 or time.perf_counter() - t_w < WARMUP_S:
+        # replays of the K-step graph: at least one, then until --warmup-s has passed
+        while n_warm < 1 or time.perf_counter() - t_w < args.warmup_s:
             g.replay()
             side.synchronize()
             n_warm += 1
@@ -326,6 +326,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10,
                     help="untimed steps before the timed ones; more of them run until at least "
                          f"{WARMUP_S} s of work has passed, so that the GPU has left its idle clocks")
+    ap.add_argument("--warmup-s", type=float, default=WARMUP_S,
+                    help="least seconds of untimed steps before the timed ones (0 for counter "
+                         "collection runs, which profile every dispatch)")
     ap.add_argument("--workload", default="mistral_bf16_chunked", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-threads", type=int, default=None,
@@ -426,7 +429,7 @@ def main():
         step()
         n_warm += 1
     torch.cuda.synchronize()
-    while time.perf_counter() - t_w < WARMUP_S:
+    while time.perf_counter() - t_w < args.warmup_s:
         for _ in range(10):
             step()
         n_warm += 10
