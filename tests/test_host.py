@@ -75,3 +75,21 @@ def test_parse_amd_smi():
     assert bench.parse_amd_smi(json.dumps([gpu]))["socket_power_w"] == 1012
     assert bench.parse_amd_smi("no output") is None
     assert bench.parse_amd_smi(json.dumps({"gpu_data": [{"gpu": 0}]})) is None
+
+
+def test_cpu_baseline_reports_parity_of_its_rows():
+    """The bench line's parity comes from the rows the CPU baseline computes:
+    the oracle's own output passes, a 1% scaled one fails the fp32 bars."""
+    import numpy as np
+
+    import oracle
+    wl = workloads.WORKLOADS["tiny_f32"]
+    x = workloads.make_inputs(wl)
+    T, sp = wl.chunks[0]
+    ref = oracle.default().attention(x.q_f32, x.k_f32, x.v_f32, T, sp, wl.num_heads,
+                                     wl.num_kv_heads, wl.head_dim)
+    base, par = bench.cpu_baseline(wl, x, 0.05, threads=2, gpu_out=[ref.astype(np.float32)])
+    assert base["kind"] == "oracle" and base["cores"] == 2 and base["value"] > 0
+    assert par["ok"] and par["max_abs"] < 1e-6 and par["rows"] > 0
+    _, bad = bench.cpu_baseline(wl, x, 0.05, threads=2, gpu_out=[(ref * 1.01).astype(np.float32)])
+    assert not bad["ok"] and bad["rel_rms"] > 5e-3
