@@ -159,6 +159,127 @@ def cpu_baseline(wl, x, target_s: float, threads: int | None = None, gpu_out=Non
     return base, parity
 
 
+def prepare_calls(wl, x, dev):
+    """Each chunk's C-ABI call of a workload with its arguments checked and
+    marshalled once (PreparedCall), over device copies of the inputs x, so
+    that a timed loop issues only the calls (µs-scale kernels would otherwise
+    wait on the host)."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
+
+    def dev_tensor(a):
+        if wl.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return t.view(torch.bfloat16 if wl.dtype == "bf16" else torch.float16)
+
+    page_kw = {}
+    if wl.ring:
+        # the cache as a ring of wl.ring slots per kv head (key j in slot j % ring),
+        # as left by writing the keys up to the chunk's last one
+        assert len(wl.chunks) == 1
+        L = wl.chunks[0][1] + wl.chunks[0][0]
+        k = dev_tensor(workloads.ring_cache(x.k_store, wl.ring, L, 0))
+        v = dev_tensor(workloads.ring_cache(x.v_store, wl.ring, L, 0))
+        kv_stride, ring_slots = wl.ring * D, wl.ring
+    elif wl.page_size:
+        # the cache as a pool of pages in scrambled order plus the sequence's page table
+        assert len(wl.chunks) == 1
+        L = wl.chunks[0][1] + wl.chunks[0][0]
+        npages = -(-L // wl.page_size) + 16
+        kp, table = workloads.paged_cache(x.k_store, wl.page_size, L, npages, wl.seed, 0)
+        vp, _ = workloads.paged_cache(x.v_store, wl.page_size, L, npages, wl.seed, 0)
+        k, v = dev_tensor(kp), dev_tensor(vp)
+        kv_stride, ring_slots = 0, None
+        page_kw = {"page_table": torch.from_numpy(table).to(dev), "page_size": wl.page_size}
+    else:
+        k = dev_tensor(x.k_store)
+        v = dev_tensor(x.v_store)
+        kv_stride, ring_slots = wl.capacity * D, None
+    calls = []
+    for ci, (T, sp) in enumerate(wl.chunks):
+        q = dev_tensor(x.q_rows(ci)[0])
+        out = torch.empty(T, H * D, dtype=torch.float32, device=dev)
+        nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
+                                     workspace=ws, ring_slots=ring_slots, **page_kw))
+    return calls
+
+
+def warm_and_time(step, sync, steps: int, warmup: int, warmup_s: float):
+    """The requested warm-up steps, then more until warmup_s seconds have
+    passed (from idle the GPU needs some tens of ms of load to reach its
+    working clock: the first 25 steps of the default workload run ~15% slower
+    than steady state); then `steps` steps back to back, timed by the wall
+    clock (job throughput) and by one pair of HIP events on the launch stream
+    (average launch time).  Returns (warm-up steps run, warm-up seconds,
+    wall seconds, stream milliseconds)."""
+    import torch
+    n_warm, t_w = 0, time.perf_counter()
+    for _ in range(warmup):
+        step()
+        n_warm += 1
+    sync()
+    while time.perf_counter() - t_w < warmup_s:
+        for _ in range(10):
+            step()
+        n_warm += 10
+        sync()
+    warm_s = time.perf_counter() - t_w
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sync()
+    t_start = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    sync()
+    return n_warm, warm_s, time.perf_counter() - t_start, e0.elapsed_time(e1)
+
+
+def other_workload(name: str, steps: int, warmup_s: float):
+    """A compact measurement of another workload in the same process (same
+    protocol, no CPU baseline): throughput, stream time per call and the
+    roofline fraction of its dtype's peak."""
+    import torch
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl)
+    calls = prepare_calls(wl, x, torch.device("cuda:0"))
+    torch.cuda.synchronize()
+
+    def step():
+        for call in calls:
+            call()
+
+    n_warm, warm_s, elapsed, gpu_ms = warm_and_time(step, torch.cuda.synchronize, steps, 10, warmup_s)
+    flops = sum(attention_flops(T, sp, wl.num_heads, wl.head_dim, wl.window) for T, sp in wl.chunks)
+    nbytes = sum(algorithmic_bytes(wl, T, sp) for T, sp in wl.chunks)
+    per_call_ms = gpu_ms / (steps * len(calls))
+    roof = roofline(wl, flops, nbytes, len(calls), per_call_ms, read_traffic(wl.name))
+    del calls, x
+    torch.cuda.empty_cache()
+    return {"value": round(flops / (elapsed / steps) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(elapsed * 1e3 / steps, 4), "stream_us_per_call": round(per_call_ms * 1e3, 2),
+            "steps": steps, "warmup_steps_run": n_warm, "description": wl.summary, "roofline": roof}
+
+
+def roofline(wl, flops_step: int, bytes_step: int, n_calls: int, mean_launch_ms: float, traffic):
+    """The dominant kernel's roofline entry: algorithmic flops per launch over
+    the average launch time on the stream, against the dtype's dense matrix
+    peak; below the ridge of that peak over HBM bandwidth (short chunks over
+    long caches) algorithmic bytes per launch against HBM instead."""
+    peak = PEAK_TFLOPS[wl.dtype]
+    if flops_step / bytes_step < peak * 1e12 / (HBM_GBS * 1e9):
+        gbs = bytes_step / n_calls / (mean_launch_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_GBS, 4), "traffic": traffic}
+    achieved = flops_step / n_calls / (mean_launch_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
 def sample_device(step, sync, samples: int = 3, load_s: float = 1.0, timeout_s: float = 30.0):
     """GPU clocks and socket power read by amd-smi while the workload runs.
 
@@ -334,6 +455,9 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=None,
                     help="oracle threads for the CPU baseline (default: every visible core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="with the default workload, skip the compact measurement of the head_dim 512 "
+                         "global layer and the sliding-window layer after the timed region")
     ap.add_argument("--no-device-sample", action="store_true",
                     help="skip reading GPU clocks and power with amd-smi after the timed steps")
     ap.add_argument("--kv-write", action="store_true",
@@ -366,46 +490,7 @@ def main():
     t0 = time.perf_counter()
     x = workloads.make_inputs(wl)
 
-    def dev_tensor(a):
-        if wl.dtype == "f32":
-            return torch.from_numpy(a).to(dev)
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-        return t.view(torch.bfloat16 if wl.dtype == "bf16" else torch.float16)
-
-    page_kw = {}
-    if wl.ring:
-        # the cache as a ring of wl.ring slots per kv head (key j in slot j % ring),
-        # as left by writing the keys up to the chunk's last one
-        assert len(wl.chunks) == 1
-        L = wl.chunks[0][1] + wl.chunks[0][0]
-        k = dev_tensor(workloads.ring_cache(x.k_store, wl.ring, L, 0))
-        v = dev_tensor(workloads.ring_cache(x.v_store, wl.ring, L, 0))
-        kv_stride, ring_slots = wl.ring * D, wl.ring
-    elif wl.page_size:
-        # the cache as a pool of pages in scrambled order plus the sequence's page table
-        assert len(wl.chunks) == 1
-        L = wl.chunks[0][1] + wl.chunks[0][0]
-        npages = -(-L // wl.page_size) + 16
-        kp, table = workloads.paged_cache(x.k_store, wl.page_size, L, npages, wl.seed, 0)
-        vp, _ = workloads.paged_cache(x.v_store, wl.page_size, L, npages, wl.seed, 0)
-        k, v = dev_tensor(kp), dev_tensor(vp)
-        kv_stride, ring_slots = 0, None
-        page_kw = {"page_table": torch.from_numpy(table).to(dev), "page_size": wl.page_size}
-    else:
-        k = dev_tensor(x.k_store)
-        v = dev_tensor(x.v_store)
-        kv_stride, ring_slots = wl.capacity * D, None
-    # each chunk's C-ABI call with its arguments checked and marshalled once, so
-    # that the timed loop issues only the calls (µs-scale kernels would
-    # otherwise wait on the host)
-    calls = []
-    for ci, (T, sp) in enumerate(wl.chunks):
-        q = dev_tensor(x.q_rows(ci)[0])
-        out = torch.empty(T, H * D, dtype=torch.float32, device=dev)
-        nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-        calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
-                                     workspace=ws, ring_slots=ring_slots, **page_kw))
+    calls = prepare_calls(wl, x, dev)
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -420,34 +505,9 @@ def main():
             if events is not None:
                 events[i][1].record()
 
-    # warm-up: the requested steps, then more until WARMUP_S seconds have
-    # passed; from idle the GPU needs some tens of ms of load to reach its
-    # working clock (measured: the first 25 steps of the default workload run
-    # ~15% slower than steady state)
-    n_warm, t_w = 0, time.perf_counter()
-    for _ in range(args.warmup):
-        step()
-        n_warm += 1
-    torch.cuda.synchronize()
-    while time.perf_counter() - t_w < args.warmup_s:
-        for _ in range(10):
-            step()
-        n_warm += 10
-        torch.cuda.synchronize()
-    warmup_s = time.perf_counter() - t_w
-
-    # timed region: K steps back to back, wall clock for the job throughput and
-    # one pair of HIP events on the launch stream for the average launch time
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    gpu_ms = e0.elapsed_time(e1)
+    # warm-up, then the timed region: K steps back to back
+    n_warm, warmup_s, elapsed, gpu_ms = warm_and_time(step, torch.cuda.synchronize, args.steps,
+                                                      args.warmup, args.warmup_s)
 
     # the outputs of the last timed step (every call writes its own buffer)
     outs = [c.out.clone() for c in calls]
@@ -472,7 +532,6 @@ def main():
     # the fused kernel (with the merge kernel when a call splits its keys):
     # algorithmic flops per launch over the average launch time on the stream
     mean_launch_ms = gpu_ms / (args.steps * len(calls))
-    achieved = flops_step / len(calls) / (mean_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     traffic = read_traffic(wl.name)
     for i, (T, sp) in enumerate(wl.chunks):
@@ -507,17 +566,17 @@ def main():
                    "flops_per_step": flops_step, "algorithmic_bytes_per_step": bytes_step,
                    "peak_fraction": round(value / peak, 4), "parallelism": "single GPU",
                    "stream_ms_per_step": round(gpu_ms / args.steps, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
+        "roofline": roofline(wl, flops_step, bytes_step, len(calls), mean_launch_ms, traffic),
     }
-    if flops_step / bytes_step < peak * 1e12 / (HBM_GBS * 1e9):
-        # below the ridge of the dtype's matrix peak over HBM bandwidth (short
-        # chunks over long caches): priced against HBM
-        gbs = bytes_step / len(calls) / (mean_launch_ms * 1e-3) / 1e9
-        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS,
-                              "unit": "GB/s", "frac": round(gbs / HBM_GBS, 4), "traffic": traffic}
     # clocks and power under the same load (after the timed region, outside it)
     result["device"] = None if args.no_device_sample else sample_device(step, torch.cuda.synchronize)
+    # the other bf16 workloads the metric's bar covers, measured the same way
+    # in the same process (after the headline's timed region, outside it)
+    if args.others and wl.name == "mistral_bf16_chunked":
+        result["other_workloads"] = {}
+        for name in ("gemma_global_bf16", "gemma_swa_bf16"):
+            result["other_workloads"][name] = other_workload(name, args.steps, args.warmup_s)
+            print(f"{name}: {result['other_workloads'][name]}", file=sys.stderr, flush=True)
     if wl.ring:
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:
