@@ -497,13 +497,9 @@ def main():
     flops_step = sum(attention_flops(T, sp, H, D, W) for T, sp in wl.chunks)
     bytes_step = sum(algorithmic_bytes(wl, T, sp) for T, sp in wl.chunks)
 
-    def step(events=None):
-        for i, call in enumerate(calls):
-            if events is not None:
-                events[i][0].record()
+    def step():
+        for call in calls:
             call()
-            if events is not None:
-                events[i][1].record()
 
     # warm-up, then the timed region: K steps back to back
     n_warm, warmup_s, elapsed, gpu_ms = warm_and_time(step, torch.cuda.synchronize, args.steps,
@@ -518,15 +514,23 @@ def main():
         identical &= all(bool(torch.equal(c.out, o)) for c, o in zip(calls, outs))
     torch.cuda.synchronize()
 
-    # diagnostics (not timed): HIP events around every call of a few steps
-    n_diag = min(args.steps, 10)
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in calls] for _ in range(n_diag)]
-    for s_ in range(n_diag):
-        step(ev[s_])
-    torch.cuda.synchronize()
-    launch_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])  # [steps, calls]
-    per_call_ms = launch_ms.mean(axis=0)
+    # diagnostics (not timed): each call's own time, from that call repeated
+    # back to back between one pair of HIP events after as many untimed
+    # repeats, about 10 ms each (events around every call of a step would add
+    # a gap to each launch)
+    per_call_ms = np.zeros(len(calls))
+    est_ms = gpu_ms / (args.steps * len(calls))
+    reps = int(min(500, max(10, 10.0 / max(est_ms, 1e-3))))
+    for i, call in enumerate(calls):
+        for _ in range(reps):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        per_call_ms[i] = a.elapsed_time(b) / reps
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops_step / (elapsed / args.steps) / 1e12
     # the fused kernel (with the merge kernel when a call splits its keys):
@@ -577,6 +581,12 @@ def main():
         for name in ("gemma_global_bf16", "gemma_swa_bf16"):
             result["other_workloads"][name] = other_workload(name, args.steps, args.warmup_s)
             print(f"{name}: {result['other_workloads'][name]}", file=sys.stderr, flush=True)
+    # each call's own time (diagnostics above, outside the timed region)
+    result["per_call"] = [{"T": T, "start_pos": sp, "us": round(ms * 1e3, 2),
+                           "mfma_frac": round(attention_flops(T, sp, H, D, W) / (ms * 1e-3) / 1e12 / peak, 4)}
+                          for (T, sp), ms in zip(wl.chunks, per_call_ms)]
+    result["per_call_how"] = (f"each call repeated {reps} times back to back between one pair of HIP events, "
+                              f"after {reps} untimed repeats")
     if wl.ring:
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:
