@@ -531,6 +531,21 @@ def main():
         b.record()
         torch.cuda.synchronize()
         per_call_ms[i] = a.elapsed_time(b) / reps
+    # and each call alone between its own pair of events, 20 times after 3
+    # untimed calls: median and minimum (this includes the gap that the
+    # events put before each launch)
+    single_ms = np.zeros((len(calls), 2))
+    for i, call in enumerate(calls):
+        for _ in range(3):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for a, b in evs:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        t_ = np.array([a.elapsed_time(b) for a, b in evs])
+        single_ms[i] = np.median(t_), t_.min()
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops_step / (elapsed / args.steps) / 1e12
     # the fused kernel (with the merge kernel when a call splits its keys):
@@ -583,10 +598,12 @@ def main():
             print(f"{name}: {result['other_workloads'][name]}", file=sys.stderr, flush=True)
     # each call's own time (diagnostics above, outside the timed region)
     result["per_call"] = [{"T": T, "start_pos": sp, "us": round(ms * 1e3, 2),
-                           "mfma_frac": round(attention_flops(T, sp, H, D, W) / (ms * 1e-3) / 1e12 / peak, 4)}
-                          for (T, sp), ms in zip(wl.chunks, per_call_ms)]
-    result["per_call_how"] = (f"each call repeated {reps} times back to back between one pair of HIP events, "
-                              f"after {reps} untimed repeats")
+                           "mfma_frac": round(attention_flops(T, sp, H, D, W) / (ms * 1e-3) / 1e12 / peak, 4),
+                           "us_alone_median": round(sm[0] * 1e3, 2), "us_alone_min": round(sm[1] * 1e3, 2)}
+                          for (T, sp), ms, sm in zip(wl.chunks, per_call_ms, single_ms)]
+    result["per_call_how"] = (f"us: each call repeated {reps} times back to back between one pair of HIP events, "
+                              f"after {reps} untimed repeats; us_alone_*: 20 calls each between its own pair "
+                              f"of events, after 3 untimed calls")
     if wl.ring:
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:
