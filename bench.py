@@ -159,11 +159,14 @@ def cpu_baseline(wl, x, target_s: float, threads: int | None = None, gpu_out=Non
     return base, parity
 
 
-def prepare_calls(wl, x, dev):
+def prepare_calls(wl, x, dev, vmirror=False):
     """Each chunk's C-ABI call of a workload with its arguments checked and
     marshalled once (PreparedCall), over device copies of the inputs x, so
     that a timed loop issues only the calls (µs-scale kernels would otherwise
-    wait on the host)."""
+    wait on the host).  vmirror: through prefill_attn_vmirror_ex with a V
+    mirror of the cache's capacity, filled up to each chunk's start by one
+    untimed call, so that each timed call rewrites only its own keys' tiles
+    (the steady state of a chunked prefill; linear caches without a window)."""
     import torch
     import causal_gqa_attention_prefill_amd as pa
     H, KVH, D, W = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.window
@@ -197,14 +200,30 @@ def prepare_calls(wl, x, dev):
         k = dev_tensor(x.k_store)
         v = dev_tensor(x.v_store)
         kv_stride, ring_slots = wl.capacity * D, None
+    mirror = None
+    if vmirror:
+        if wl.ring or wl.page_size or W:
+            raise ValueError("the V mirror serves linear caches without a window")
+        mb = pa.vmirror_bytes(wl.dtype, KVH, D, wl.capacity)
+        if mb == 0:
+            raise ValueError(f"{wl.name}: no kernel of this dtype and head_dim reads a V mirror")
+        mirror = torch.empty(mb, dtype=torch.uint8, device=dev)
     calls = []
     for ci, (T, sp) in enumerate(wl.chunks):
         q = dev_tensor(x.q_rows(ci)[0])
         out = torch.empty(T, H * D, dtype=torch.float32, device=dev)
         nb = pa.workspace_bytes(wl.dtype, T, sp, H, KVH, D, W)
         ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-        calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
-                                     workspace=ws, ring_slots=ring_slots, **page_kw))
+        if mirror is not None:
+            mkw = {"v_mirror": mirror, "mirror_capacity": wl.capacity}
+            # the keys before the chunk, as earlier chunks would have left them
+            pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W, workspace=ws,
+                            mirror_keys=0, **mkw)()
+            calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
+                                         workspace=ws, mirror_keys=sp, **mkw))
+        else:
+            calls.append(pa.PreparedCall(q, H * D, k, v, kv_stride, out, H * D, T, sp, H, KVH, D, W,
+                                         workspace=ws, ring_slots=ring_slots, **page_kw))
     return calls
 
 
@@ -239,14 +258,14 @@ def warm_and_time(step, sync, steps: int, warmup: int, warmup_s: float):
     return n_warm, warm_s, time.perf_counter() - t_start, e0.elapsed_time(e1)
 
 
-def other_workload(name: str, steps: int, warmup_s: float):
+def other_workload(name: str, steps: int, warmup_s: float, vmirror: bool = False):
     """A compact measurement of another workload in the same process (same
     protocol, no CPU baseline): throughput, stream time per call and the
     roofline fraction of its dtype's peak."""
     import torch
     wl = workloads.WORKLOADS[name]
     x = workloads.make_inputs(wl)
-    calls = prepare_calls(wl, x, torch.device("cuda:0"))
+    calls = prepare_calls(wl, x, torch.device("cuda:0"), vmirror)
     torch.cuda.synchronize()
 
     def step():
@@ -257,7 +276,8 @@ def other_workload(name: str, steps: int, warmup_s: float):
     flops = sum(attention_flops(T, sp, wl.num_heads, wl.head_dim, wl.window) for T, sp in wl.chunks)
     nbytes = sum(algorithmic_bytes(wl, T, sp) for T, sp in wl.chunks)
     per_call_ms = gpu_ms / (steps * len(calls))
-    roof = roofline(wl, flops, nbytes, len(calls), per_call_ms, read_traffic(wl.name))
+    roof = roofline(wl, flops, nbytes, len(calls), per_call_ms,
+                    read_traffic(wl.name + ("+vmirror" if vmirror else "")))
     del calls, x
     torch.cuda.empty_cache()
     return {"value": round(flops / (elapsed / steps) / 1e12, 2), "unit": "TFLOP/s",
@@ -455,6 +475,9 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=None,
                     help="oracle threads for the CPU baseline (default: every visible core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vmirror", action="store_true",
+                    help="call prefill_attn_vmirror_ex with a V mirror filled up to each chunk's start "
+                         "(head_dim 512 bf16/fp16 workloads without a window)")
     ap.add_argument("--no-others", dest="others", action="store_false",
                     help="with the default workload, skip the compact measurement of the head_dim 512 "
                          "global layer and the sliding-window layer after the timed region")
@@ -490,7 +513,7 @@ def main():
     t0 = time.perf_counter()
     x = workloads.make_inputs(wl)
 
-    calls = prepare_calls(wl, x, dev)
+    calls = prepare_calls(wl, x, dev, args.vmirror)
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -552,7 +575,7 @@ def main():
     # algorithmic flops per launch over the average launch time on the stream
     mean_launch_ms = gpu_ms / (args.steps * len(calls))
     peak = PEAK_TFLOPS[wl.dtype]
-    traffic = read_traffic(wl.name)
+    traffic = read_traffic(wl.name + ("+vmirror" if args.vmirror else ""))
     for i, (T, sp) in enumerate(wl.chunks):
         f = attention_flops(T, sp, H, D, W)
         b = algorithmic_bytes(wl, T, sp)
@@ -593,9 +616,11 @@ def main():
     # in the same process (after the headline's timed region, outside it)
     if args.others and wl.name == "mistral_bf16_chunked":
         result["other_workloads"] = {}
-        for name in ("gemma_global_bf16", "gemma_swa_bf16"):
-            result["other_workloads"][name] = other_workload(name, args.steps, args.warmup_s)
-            print(f"{name}: {result['other_workloads'][name]}", file=sys.stderr, flush=True)
+        for name, vm in (("gemma_global_bf16", False), ("gemma_swa_bf16", False),
+                         ("gemma_global_bf16", True)):
+            key = name + ("+vmirror" if vm else "")
+            result["other_workloads"][key] = other_workload(name, args.steps, args.warmup_s, vm)
+            print(f"{key}: {result['other_workloads'][key]}", file=sys.stderr, flush=True)
     # each call's own time (diagnostics above, outside the timed region)
     result["per_call"] = [{"T": T, "start_pos": sp, "us": round(ms * 1e3, 2),
                            "mfma_frac": round(attention_flops(T, sp, H, D, W) / (ms * 1e-3) / 1e12 / peak, 4),
@@ -604,6 +629,8 @@ def main():
     result["per_call_how"] = (f"us: each call repeated {reps} times back to back between one pair of HIP events, "
                               f"after {reps} untimed repeats; us_alone_*: 20 calls each between its own pair "
                               f"of events, after 3 untimed calls")
+    if args.vmirror:
+        result["config"]["entry_point"] = "prefill_attn_vmirror_ex (V mirror filled up to the chunk's start)"
     if wl.ring:
         result["config"]["ring_slots"] = wl.ring
     if wl.page_size:

@@ -55,6 +55,11 @@ def load():
     lib.prefill_attn_ex.restype = I
     lib.prefill_attn_noalloc_ex.argtypes = [I, P, I64, P, P, I64, P, I64, I, I, I, I, I, I, I, P]
     lib.prefill_attn_noalloc_ex.restype = I
+    lib.prefill_attn_vmirror_ex.argtypes = [I, P, I64, P, P, I64, P, I, I, P, I64, I, I, I, I, I, I, P,
+                                            SZ, P]
+    lib.prefill_attn_vmirror_ex.restype = I
+    lib.prefill_attn_vmirror_bytes.argtypes = [I, I, I, I]
+    lib.prefill_attn_vmirror_bytes.restype = SZ
     lib.prefill_attn_ring_ex.argtypes = [I, P, I64, P, P, I64, I, P, I64, I, I, I, I, I, I, I, P, SZ,
                                          P]
     lib.prefill_attn_ring_ex.restype = I
@@ -101,6 +106,11 @@ def strerror(status: int) -> str:
 def workspace_bytes(dtype: str, T, start_pos, num_heads, num_kv_heads, head_dim, window=0) -> int:
     return int(load().prefill_attn_workspace_bytes(DTYPE_CODES[dtype], T, start_pos, num_heads,
                                                    num_kv_heads, head_dim, window))
+
+
+def vmirror_bytes(dtype: str, num_kv_heads, head_dim, capacity) -> int:
+    """Bytes of the V mirror prefill_attn_vmirror_ex reads (0: not needed)."""
+    return int(load().prefill_attn_vmirror_bytes(DTYPE_CODES[dtype], num_kv_heads, head_dim, capacity))
 
 
 def plan(dtype: str, T, start_pos, num_heads, num_kv_heads, head_dim, window=0) -> dict:
@@ -164,9 +174,10 @@ def prefill_attn(q, k_cache, v_cache, out, T, start_pos, num_heads, num_kv_heads
 
 
 class PreparedCall:
-    """prefill_attn_ex (prefill_attn_ring_ex when ring_slots is given) with
-    its arguments checked and marshalled once.  out may be float32, bfloat16
-    or float16 (out_dtype follows its dtype).
+    """prefill_attn_ex (prefill_attn_ring_ex when ring_slots is given, the
+    paged forms with a page table, prefill_attn_vmirror_ex with a v_mirror)
+    with its arguments checked and marshalled once.  out may be float32,
+    bfloat16 or float16 (out_dtype follows its dtype).
 
     For callers that launch the same call repeatedly (a chunk loop, a
     benchmark): calling the object issues just the C-ABI call.  The tensors
@@ -176,7 +187,7 @@ class PreparedCall:
     def __init__(self, q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
                  start_pos, num_heads, num_kv_heads, head_dim, window=0, workspace=None,
                  stream=None, ring_slots=None, page_table=None, page_size=None,
-                 start_pos_dev=None):
+                 start_pos_dev=None, v_mirror=None, mirror_capacity=None, mirror_keys=0):
         dt = _dtype_of(q)
         if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
             raise TypeError("q, k_cache and v_cache must share one storage type")
@@ -203,7 +214,20 @@ class PreparedCall:
                 v_cache.data_ptr(), kv_head_stride)
         tail = (out.data_ptr(), out_row_stride, out_dt, T, start_pos, num_heads, num_kv_heads,
                 head_dim, window, ws_ptr, ws_bytes, _stream(stream))
-        if start_pos_dev is not None:
+        if v_mirror is not None:
+            if ring_slots is not None or page_table is not None or window != 0:
+                raise ValueError("the V mirror serves linear caches without a window")
+            if not v_mirror.is_cuda or not v_mirror.is_contiguous():
+                raise ValueError("v_mirror must be a contiguous device tensor")
+            nb = vmirror_bytes(dt, num_kv_heads, head_dim, mirror_capacity)
+            if v_mirror.numel() * v_mirror.element_size() < nb:
+                raise ValueError(f"v_mirror holds {v_mirror.numel() * v_mirror.element_size()} bytes, "
+                                 f"the call needs {nb}")
+            self._name, self._fn = "prefill_attn_vmirror_ex", load().prefill_attn_vmirror_ex
+            self._args = head + (v_mirror.data_ptr(), int(mirror_capacity), int(mirror_keys)) + \
+                (out.data_ptr(), out_row_stride, out_dt, T, start_pos, num_heads, num_kv_heads,
+                 head_dim, ws_ptr, ws_bytes, _stream(stream))
+        elif start_pos_dev is not None:
             # start_pos is the largest the device value may take
             import torch
             if page_table is None or start_pos_dev.dtype != torch.int32:
@@ -227,7 +251,7 @@ class PreparedCall:
         else:
             self._name, self._fn = "prefill_attn_ring_ex", load().prefill_attn_ring_ex
             self._args = head + (int(ring_slots),) + tail
-        self._keep = (q, k_cache, v_cache, out, workspace, page_table, start_pos_dev)
+        self._keep = (q, k_cache, v_cache, out, workspace, page_table, start_pos_dev, v_mirror)
         self.out = out
 
     def __call__(self):
@@ -266,6 +290,18 @@ def prefill_attn_noalloc_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, o
     if st != PA_OK:
         raise PrefillAttnError(st, "prefill_attn_noalloc_ex")
     return out
+
+
+def prefill_attn_vmirror_ex(q, q_row_stride, k_cache, v_cache, kv_head_stride, v_mirror,
+                            mirror_capacity, mirror_keys, out, out_row_stride, T, start_pos, num_heads,
+                            num_kv_heads, head_dim, workspace=None, stream=None):
+    """Causal call (no window) that keeps V's operand-order copy in v_mirror
+    (a device tensor of vmirror_bytes(...) bytes) across the chunks of a
+    sequence: keys 0 .. mirror_keys-1 are already in it, the call adds the
+    rest up to start_pos+T."""
+    return PreparedCall(q, q_row_stride, k_cache, v_cache, kv_head_stride, out, out_row_stride, T,
+                        start_pos, num_heads, num_kv_heads, head_dim, 0, workspace, stream,
+                        v_mirror=v_mirror, mirror_capacity=mirror_capacity, mirror_keys=mirror_keys)()
 
 
 def prefill_attn_ring_ex(q, q_row_stride, k_ring, v_ring, kv_head_stride, ring_slots, out,

@@ -107,6 +107,7 @@ struct Params {
     const uint16_t *vop;   // V of the call's KV tiles in MFMA operand order (16-bit kernels)
     int vop_kt_lo;         // first KV tile held in vop
     int vop_tiles;         // KV tiles per kv head held in vop
+    int vop_pack0;         // first tile of vop (from vop_kt_lo) the pass rewrites this call
 };
 
 // A call whose start_pos sits in device memory (so that one captured graph
@@ -584,7 +585,10 @@ struct Ones {
 // 64 + lane holds the 8 values that lane feeds to one MFMA, so the attention
 // kernels copy tiles into LDS verbatim and read each operand with one
 // contiguous ds_read_b128.  Keys no row of the call reads (at or past L,
-// below the first query's window) are written as zeros.
+// below the first query's window) are written as zeros.  The copy is either
+// per call (in the workspace, the call's tiles) or a mirror the caller keeps
+// across the chunks of a sequence (key 0 up; each call rewrites only the
+// tiles from the first key the mirror lacks, grid x = tiles rewritten).
 //   M32 (32x32x16 MFMA): block = 32-wide d block, step = 16 keys; lane
 //        (l%32, l/32), element e: key 16*step + 8*(e/4) + 4*(l/32) + e%4,
 //        d = 32*block + l%32
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(256) void pack_v_operands(Params p, uint16_t *vop) 
     constexpr int CHUNKS = BK * D / 8;
     __shared__ uint32_t t32[BK * PITCH / 2];
     const uint16_t *t16 = (const uint16_t *)t32;
-    const int tile = blockIdx.x, kvh = blockIdx.y;
+    const int tile = p.vop_pack0 + blockIdx.x, kvh = blockIdx.y;
     const int j0 = (kt_lo + tile) * BK;
     for (int cidx = threadIdx.x; cidx < CHUNKS; cidx += 256) {
         const int key = cidx / (D / 8), c8 = cidx % (D / 8);
@@ -1851,8 +1855,10 @@ struct Plan {
     const Variant *var;
     int G, TQ, nq, S, items;
     int64_t tiles;               // KV tiles visited by all work-groups
-    int vop_kt_lo, vop_tiles;    // KV tiles rewritten in operand order (16-bit inputs)
-    size_t vop_bytes;            // their bytes, at the start of the workspace
+    int vop_kt_lo, vop_tiles;    // KV tiles held in operand order (16-bit inputs)
+    size_t vop_bytes;            // their bytes, at the start of the workspace (0 with a mirror)
+    void *vmirror = nullptr;     // the caller's operand-order copy of V (else the workspace)
+    int pack0 = 0, npack = 0;    // tiles (from vop_kt_lo) the operand-order pass rewrites
     size_t ws_bytes, ws_o_offset, ws_ml_offset;
 };
 
@@ -1916,7 +1922,7 @@ int choose_splits(const Variant &var, int T, int start_pos, int H, int KVH, int 
 }
 
 int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window, Plan *pl,
-              bool no_pack = false, int max_splits = kMaxSplits) {
+              bool no_pack = false, int max_splits = kMaxSplits, bool mirror = false) {
     const int st = check_shape(dtype, T, start_pos, H, KVH, D, window);
     if (st != PA_OK) return st;
     const Variant *var = find_variant(dtype, D);
@@ -1932,7 +1938,9 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     // draft verification) read V in place.
     // (a start_pos known only on the device also reads V in place: the copy
     // covers the call's tiles, which the host plan cannot know)
-    if (var->pack && (no_pack || cdiv(T, var->rows / (H / KVH)) < kMinQueryTilesForPack))
+    // (with the caller's mirror of that copy only the new tiles are rewritten,
+    // so the operand-order variant serves every chunk length)
+    if (var->pack && !mirror && (no_pack || cdiv(T, var->rows / (H / KVH)) < kMinQueryTilesForPack))
         if (const Variant *alt = find_ksplit_variant(dtype, D, 0)) var = alt;
     pl->var = var;
     pl->G = H / KVH;
@@ -1968,12 +1976,15 @@ int make_plan(int dtype, int T, int start_pos, int H, int KVH, int D, int window
     pl->vop_kt_lo = 0;
     pl->vop_tiles = 0;
     pl->vop_bytes = 0;
-    if (var->pack) {
+    pl->vmirror = nullptr;
+    pl->pack0 = pl->npack = 0;
+    if (var->pack && !mirror) {
         pl->vop_kt_lo = first_key_host(start_pos, window) / var->BK;
         pl->vop_tiles = (int)(((int64_t)start_pos + T - 1) / var->BK + 1 - pl->vop_kt_lo);
         const int64_t tile_bytes = (int64_t)var->BK * D * 2;
         if ((int64_t)pl->vop_tiles * tile_bytes > INT32_MAX) return PA_ERR_UNSUPPORTED;
         pl->vop_bytes = (size_t)(((int64_t)KVH * pl->vop_tiles * tile_bytes + 255) & ~(int64_t)255);
+        pl->npack = pl->vop_tiles;
     }
     pl->ws_o_offset = pl->vop_bytes;
     pl->ws_ml_offset = pl->vop_bytes;
@@ -2011,9 +2022,11 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.out_dtype = out_dtype;
     p.ws_o = pl.S > 1 ? (float *)((char *)ws + pl.ws_o_offset) : nullptr;
     p.ws_ml = pl.S > 1 ? (float2 *)((char *)ws + pl.ws_ml_offset) : nullptr;
-    p.vop = pl.var->pack ? (const uint16_t *)ws : nullptr;
+    uint16_t *const vop = pl.var->pack ? (uint16_t *)(pl.vmirror ? pl.vmirror : ws) : nullptr;
+    p.vop = vop;
     p.vop_kt_lo = pl.vop_kt_lo;
     p.vop_tiles = pl.vop_tiles;
+    p.vop_pack0 = pl.pack0;
     p.q_row_stride = q_row_stride;
     p.kv_head_stride = kv_head_stride;
     p.out_row_stride = out_row_stride;
@@ -2038,9 +2051,8 @@ int launch(const Plan &pl, int dtype, const void *q, int64_t q_row_stride, const
     p.start_pos_dev = lay.start_pos_dev;
     p.kv_bytes = (int)std::min<int64_t>((ring ? (int64_t)ring : (int64_t)start_pos + T) * D *
                                             elem_bytes(dtype), INT32_MAX);
-    if (pl.var->pack) {
-        hipLaunchKernelGGL(pl.var->pack, dim3(pl.vop_tiles, KVH), dim3(256), 0, stream, p,
-                           (uint16_t *)ws);
+    if (pl.var->pack && pl.npack > 0) {
+        hipLaunchKernelGGL(pl.var->pack, dim3(pl.npack, KVH), dim3(256), 0, stream, p, vop);
         if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
     }
     const KernelFn fn = lay.page_table ? pl.var->fn_paged : ring ? pl.var->fn_ring : pl.var->fn;
@@ -2241,6 +2253,55 @@ int prefill_attn_ex(int dtype, const void *q, int64_t q_row_stride, const void *
     return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
                   out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, window, workspace,
                   workspace_bytes, stream);
+}
+
+size_t prefill_attn_vmirror_bytes(int dtype, int num_kv_heads, int head_dim, int capacity) {
+    if (num_kv_heads < 1 || capacity < 1) return 0;
+    const Variant *var = find_variant(dtype, head_dim);
+    if (!var || !var->pack) return 0;
+    // one kv head's tiles are addressed with 32-bit buffer offsets
+    const int64_t per_head = cdiv(capacity, var->BK) * var->BK * head_dim * 2;
+    if (per_head > kMaxHeadBytes) return 0;
+    return (size_t)num_kv_heads * (size_t)per_head;
+}
+
+int prefill_attn_vmirror_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_cache,
+                            const void *v_cache, int64_t kv_head_stride, void *v_mirror,
+                            int mirror_capacity, int mirror_keys, void *out, int64_t out_row_stride,
+                            int out_dtype, int T, int start_pos, int num_heads, int num_kv_heads,
+                            int head_dim, void *workspace, size_t workspace_bytes, void *stream) {
+    const int64_t L = (int64_t)start_pos + T;
+    int st = check_args(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, L, out,
+                        out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, 0);
+    if (st != PA_OK) return st;
+    // no kernel of this dtype and head_dim reads V in operand order: the
+    // mirror plays no part (prefill_attn_ex with window 0)
+    if (!find_variant(dtype, head_dim)->pack)
+        return run_ex(dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
+                      out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, 0,
+                      workspace, workspace_bytes, stream);
+    if (!v_mirror || mirror_capacity < L || mirror_keys < 0 || mirror_keys > L) return PA_ERR_INVALID_ARG;
+    if (!aligned16(v_mirror) || prefill_attn_vmirror_bytes(dtype, num_kv_heads, head_dim, mirror_capacity) == 0)
+        return PA_ERR_UNSUPPORTED;
+    Plan pl;
+    st = make_plan(dtype, T, start_pos, num_heads, num_kv_heads, head_dim, 0, &pl, false, kMaxSplits, true);
+    if (st != PA_OK) return st;
+    if (!pl.var->pack) return PA_ERR_UNSUPPORTED;
+    const int BK = pl.var->BK;
+    pl.vmirror = v_mirror;
+    pl.vop_kt_lo = 0;
+    pl.vop_tiles = (int)cdiv(mirror_capacity, BK);
+    // from the tile of the first key the mirror lacks through the call's last
+    // tile, which is always rewritten (its keys past L become zeros)
+    pl.pack0 = (int)(std::min<int64_t>(mirror_keys, L - 1) / BK);
+    pl.npack = (int)(cdiv(L, BK) - pl.pack0);
+    if (pl.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255) != 0) return PA_ERR_WORKSPACE;
+    }
+    return launch(pl, dtype, q, q_row_stride, k_cache, v_cache, kv_head_stride, CacheLayout{}, out,
+                  out_row_stride, out_dtype, T, start_pos, num_heads, num_kv_heads, head_dim, 0, workspace,
+                  (hipStream_t)stream);
 }
 
 int prefill_attn_noalloc_ex(int dtype, const void *q, int64_t q_row_stride, const void *k_cache,

@@ -155,6 +155,56 @@ int prefill_attn_noalloc_ex(int dtype, const void *q, int64_t q_row_stride,
                             int window, void *stream);
 
 /*
+ * prefill_attn_ex without a window, for the chunks of one long sequence in
+ * turn (the TensorSharp page "Design: closing the Gemma-4 long-prompt prefill
+ * gap", section 2: the head_dim 512 global layers prefilled as 2048-token
+ * chunks over tens of thousands of cached keys), with a mirror of V that the
+ * caller keeps.  At head_dim 512 with bf16/fp16 inputs the kernels read V in
+ * matrix-core operand order; prefill_attn_ex rewrites every V row the call
+ * reads into that order in its workspace on every call (a pass over the whole
+ * cache per chunk).  Here the rewritten tiles live in v_mirror across calls
+ * and each call rewrites only the keys the mirror lacks.
+ *   v_mirror         device memory of prefill_attn_vmirror_bytes(dtype,
+ *                    num_kv_heads, head_dim, mirror_capacity) bytes, 16-byte
+ *                    aligned, owned by the caller; its layout is the
+ *                    library's own (tiles of keys in operand order per kv head)
+ *   mirror_capacity  keys it can hold (>= start_pos + T)
+ *   mirror_keys      keys 0 .. mirror_keys-1 that it already holds: written
+ *                    by earlier calls of this function for the same v_cache,
+ *                    whose rows 0 .. mirror_keys-1 have not changed since
+ *                    (0 <= mirror_keys <= start_pos + T; 0 rewrites all)
+ * After the call's work has run, the mirror holds keys 0 .. start_pos+T-1, so
+ * the next chunk of the sequence passes mirror_keys = start_pos + T.  Calls
+ * that use one mirror must be ordered (one stream, or synchronised), as must
+ * any work that writes the rows of v_cache the mirror holds.  The result bits
+ * are those of prefill_attn_ex for the same arguments whenever that call
+ * rewrites V too (at least 8 query tiles); for shorter chunks, which it runs
+ * on V in place, they agree to rounding.  The workspace is the one
+ * prefill_attn_workspace_bytes gives for the same arguments (an upper
+ * bound: the V copy it counts is not used).  For a dtype and head_dim whose
+ * kernels read V in place (prefill_attn_vmirror_bytes returns 0) the call is
+ * prefill_attn_ex with window 0 and v_mirror is not touched.  Errors as for
+ * prefill_attn_ex, plus PA_ERR_INVALID_ARG for a null v_mirror,
+ * mirror_capacity < start_pos + T or mirror_keys outside [0, start_pos + T],
+ * and PA_ERR_UNSUPPORTED for a misaligned v_mirror or a capacity whose
+ * mirror has no size (see below).
+ */
+int prefill_attn_vmirror_ex(int dtype, const void *q, int64_t q_row_stride,
+                            const void *k_cache, const void *v_cache, int64_t kv_head_stride,
+                            void *v_mirror, int mirror_capacity, int mirror_keys,
+                            void *out, int64_t out_row_stride, int out_dtype,
+                            int T, int start_pos, int num_heads, int num_kv_heads, int head_dim,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of the V mirror prefill_attn_vmirror_ex reads for `capacity` keys;
+ * 0 when no kernel of this dtype and head_dim reads one (then the mirror is
+ * not needed), for invalid arguments, and when one kv head's share would
+ * pass 2 GiB.
+ */
+size_t prefill_attn_vmirror_bytes(int dtype, int num_kv_heads, int head_dim, int capacity);
+
+/*
  * Ring cache form (sliding-window layers).  The TensorSharp page "Design:
  * closing the Gemma-4 long-prompt prefill gap", section 4, requirement R4,
  * has sliding-window layers write the K/V of position pos into slot

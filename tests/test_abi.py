@@ -20,7 +20,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"prefill_attn_f32", "prefill_attn_bf16", "prefill_attn_f16",
                           "prefill_attn_ex", "prefill_attn_ring_ex", "prefill_attn_workspace_bytes",
                           "prefill_attn_plan", "prefill_attn_strerror", "prefill_kv_write",
-                          "prefill_attn_paged_ex", "prefill_attn_paged_dev_ex", "prefill_attn_noalloc_ex"}
+                          "prefill_attn_paged_ex", "prefill_attn_paged_dev_ex", "prefill_attn_noalloc_ex",
+                          "prefill_attn_vmirror_ex", "prefill_attn_vmirror_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -286,3 +287,31 @@ def test_noalloc_arguments(lib):
     assert call(D=48) == U and call(dt=7) == U and call(odt=9) == U
     assert call(q=FAKE + 8) == U             # misaligned
     assert pa.header_define("PA_NOALLOC_SCRATCH_BYTES") == 32 << 20
+
+
+def test_vmirror_arguments(lib):
+    """The V-mirror form checks its arguments before anything is enqueued
+    (nothing here touches a GPU); the mirror's size follows its tiles."""
+    E, U = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    fn = lib.prefill_attn_vmirror_ex
+    BF = pa.PA_DTYPE_BF16
+
+    def call(q=FAKE, qs=4 * 512, k=FAKE, v=FAKE, kvs=64 * 512, mir=FAKE, cap=64, mk=0, out=FAKE,
+             os_=4 * 512, odt=0, T=4, sp=60, H=4, KVH=2, D=512, dt=BF):
+        return fn(dt, q, qs, k, v, kvs, mir, cap, mk, out, os_, odt, T, sp, H, KVH, D, None, 0, None)
+
+    assert call(q=None) == E and call(k=None) == E and call(out=None) == E
+    assert call(T=0) == E and call(sp=-1) == E and call(H=6, KVH=4) == E
+    assert call(kvs=63 * 512) == E            # kv-head stride below L * D
+    assert call(mir=None) == E                # a mirror is needed at head_dim 512
+    assert call(cap=63) == E                  # capacity below L
+    assert call(mk=-1) == E and call(mk=65) == E
+    assert call(mir=FAKE + 8) == U            # misaligned mirror
+    assert call(D=48) == U and call(dt=7) == U
+    # sizes: whole 32-key tiles of 512 bf16 values per kv head
+    assert pa.vmirror_bytes("bf16", 2, 512, 64) == 2 * 64 * 512 * 2
+    assert pa.vmirror_bytes("f16", 2, 512, 65) == 2 * 96 * 512 * 2
+    assert pa.vmirror_bytes("bf16", 2, 128, 64) == 0      # read in place: no mirror
+    assert pa.vmirror_bytes("f32", 2, 512, 64) == 0
+    assert pa.vmirror_bytes("bf16", 0, 512, 64) == 0 and pa.vmirror_bytes("bf16", 2, 512, 0) == 0
+    assert pa.vmirror_bytes("bf16", 1, 512, 3 << 20) == 0  # one head's share would pass 2 GiB
