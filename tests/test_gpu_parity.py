@@ -274,6 +274,7 @@ VARIANTS = [
     ("fp32", "f32", 32, 8, 128, 300, 200, 0, "linear", {"waves_per_workgroup": 4}),
     ("ring", "bf16", 8, 4, 256, 512, 3000, 700, "ring", {}),
     ("paged", "bf16", 8, 2, 512, 4, 3000, 0, "paged", {}),
+    ("V mirror", "bf16", 8, 2, 512, 100, 3000, 0, "vmirror", {}),
 ]
 
 
@@ -298,6 +299,14 @@ def test_deterministic(orc, case):
     if layout == "linear":
         call = pa.PreparedCall(q, H * D, to_device(x.k_store, dtype), to_device(x.v_store, dtype), L * D,
                                out, H * D, T, sp, H, KVH, D, W, workspace=ws)
+    elif layout == "vmirror":
+        k, v = to_device(x.k_store, dtype), to_device(x.v_store, dtype)
+        mirror = torch.empty(pa.vmirror_bytes(dtype, KVH, D, L), dtype=torch.uint8, device=device())
+        # the keys before the chunk, as earlier chunks would have left them
+        pa.PreparedCall(q, H * D, k, v, L * D, out, H * D, T, sp, H, KVH, D, W, workspace=ws,
+                        v_mirror=mirror, mirror_capacity=L, mirror_keys=0)()
+        call = pa.PreparedCall(q, H * D, k, v, L * D, out, H * D, T, sp, H, KVH, D, W, workspace=ws,
+                               v_mirror=mirror, mirror_capacity=L, mirror_keys=sp)
     elif layout == "ring":
         R = W + T - 1
         call = pa.PreparedCall(q, H * D, to_device(workloads.ring_cache(x.k_store, R, L, 0), dtype),
