@@ -127,3 +127,59 @@ def test_graph_replay_over_lengths(orc):
             assert torch.equal(out, out_host), sp
         else:
             assert_parity(out_host.cpu().numpy().reshape(T, H, D), ref, "bf16", f"host start {sp}")
+
+
+def test_graph_replay_of_vmirror_loop(orc):
+    """The same kind of loop at head_dim 512 through the V mirror (each chunk
+    passes its start as mirror_keys, so the graph also rewrites the mirror's
+    new tiles): replays give the eager bits, and the eager results match the
+    oracle."""
+    import torch
+    import causal_gqa_attention_prefill_amd as pa
+    pa.load()
+    H, KVH, D, N = 8, 2, 512, 1100
+    x = workloads.make_random(H, KVH, D, N, 0, std=0.5, seed=37, dtype="bf16")
+    ref = orc.attention(x.q_f32, x.k_f32, x.v_f32, N, 0, H, KVH, D)
+    k = to_device(x.k_store, "bf16")
+    v = to_device(x.v_store, "bf16")
+    mirror = torch.empty(pa.vmirror_bytes("bf16", KVH, D, N), dtype=torch.uint8, device=device())
+    side = torch.cuda.Stream()
+    chunks = [(256, 0), (300, 256), (520, 556), (24, 1076)]
+    calls, outs = [], []
+    for T, sp in chunks:
+        q = to_device(x.q_store[sp:sp + T], "bf16")
+        out = torch.empty(T, H * D, device=device())
+        nb = pa.workspace_bytes("bf16", T, sp, H, KVH, D, 0)
+        ws = torch.empty(nb, dtype=torch.uint8, device=device()) if nb else None
+        calls.append(pa.PreparedCall(q, H * D, k, v, N * D, out, H * D, T, sp, H, KVH, D, 0,
+                                     workspace=ws, stream=side, v_mirror=mirror, mirror_capacity=N,
+                                     mirror_keys=sp))
+        outs.append(out)
+
+    def loop():
+        for c in calls:
+            c()
+
+    with torch.cuda.stream(side):
+        loop()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for (T, sp), o in zip(chunks, eager):
+        assert_parity(o.cpu().numpy().reshape(T, H, D), ref[sp:sp + T], "bf16", f"vmirror eager chunk at {sp}",
+                      group="graph")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        loop()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        with torch.cuda.stream(side):
+            for o in outs:
+                o.fill_(float("nan"))
+            g.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, eager)):
+            assert torch.equal(o, e), f"replay {rep}, chunk {i}"
+        with torch.cuda.stream(side):   # eager work between replays
+            loop()
+        torch.cuda.synchronize()
