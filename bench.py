@@ -14,7 +14,11 @@ stream around the timed steps; ``cpu_baseline`` times the fp64 oracle on a
 bounded sample of the same workload on the host cores, and compares the GPU
 output of those rows with the oracle's (``parity``).  ``determinism`` reruns
 the step five times after the timed region and compares the outputs bit for
-bit.  Diagnostics (per-call events over a few extra steps) go to stderr.
+bit.  After the timed region: ``per_call`` gives each call's own time
+(repeated back to back, and alone between its own events); with the default
+workload, ``other_workloads`` times the head_dim 512 global layer (with and
+without the V mirror) and the sliding-window layer the same way, each with
+its own roofline entry.  Diagnostics go to stderr.
 
 Warm-up: the --warmup steps (default 10), then more of the same untimed steps
 until at least WARMUP_S seconds of them have run, so that the GPU has left its
