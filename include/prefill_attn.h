@@ -5,7 +5,7 @@
  * The operation (gnosis handoff page "Prefill attention -> GPU: handoff",
  * section "GPU design (the real fix)"):
  *
- *   A chunk of T query tokens at absolute positions start_pos .. start_pos+T-1
+ *   A chunk of T query tokens, at sequence positions start_pos .. start_pos+T-1,
  *   attends to the L = start_pos + T keys held in a KV cache.  Query head h
  *   reads kv head h / (num_heads / num_kv_heads) (grouped-query attention).
  *   For query token t (position pos = start_pos + t) and each valid key j:
