@@ -11,7 +11,7 @@
 //
 // That page's plan materialises the [heads x Tq x L] scores between two
 // strided-batched GEMMs and a softmax kernel, and its "Implementation status"
-// lists fusing the softmax into the AV step as a follow-up.  Here everything
+// lists merging the softmax into the A.V product as a follow-up.  Here everything
 // is one pass over the keys (online softmax), so scores never leave
 // registers:
 //

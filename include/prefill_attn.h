@@ -7,7 +7,7 @@
  *
  *   A chunk of T query tokens, at sequence positions start_pos .. start_pos+T-1,
  *   attends to the L = start_pos + T keys held in a KV cache.  Query head h
- *   reads kv head h / (num_heads / num_kv_heads) (grouped-query attention).
+ *   uses kv head h / (num_heads / num_kv_heads) (grouped-query attention).
  *   For query token t (position pos = start_pos + t) and each valid key j:
  *       s_j = (q_t . k_j) / sqrt(head_dim)
  *   valid keys are j <= pos (causal mask, Step 2 of that section) and, when

@@ -9,15 +9,15 @@
  * What is computed.  The definition is the one in the gnosis handoff page
  * "Prefill attention -> GPU: handoff", section "GPU design (the real fix)":
  *
- *   - a chunk of T query tokens sits at absolute positions
- *     start_pos .. start_pos+T-1 and sees L = start_pos + T cached keys;
+ *   - the chunk's T query tokens are at sequence positions
+ *     start_pos .. start_pos+T-1 and see L = start_pos + T cached keys;
  *   - grouped-query attention: num_kv_groups = num_heads / num_kv_heads and
- *     query head h reads kv head h / num_kv_groups;
+ *     query head h uses kv head h / num_kv_groups;
  *   - scores are the dot product q.k multiplied by 1/sqrt(head_dim), the scale
  *     being applied before the row maximum and the softmax (Step 2);
  *   - key j is valid for query t only when j <= start_pos + t; masked keys
- *     contribute exactly nothing, like the CPU loop that only sums keys
- *     0..=pos (Step 2, and "What already shipped": the per-(token, head)
+ *     contribute exactly nothing, as in the page's CPU loop, whose sum runs
+ *     over keys 0..=pos only (Step 2, and "What already shipped": the per-(token, head)
  *     loop over the causal range 0..=pos);
  *   - row softmax, then the probability-weighted sum of the value rows
  *     (Step 3).
