@@ -93,3 +93,26 @@ def test_cpu_baseline_reports_parity_of_its_rows():
     assert par["ok"] and par["max_abs"] < 1e-6 and par["rows"] > 0
     _, bad = bench.cpu_baseline(wl, x, 0.05, threads=2, gpu_out=[(ref * 1.01).astype(np.float32)])
     assert not bad["ok"] and bad["rel_rms"] > 5e-3
+
+
+def test_source_digest_keys_traffic_records_to_code(tmp_path, monkeypatch):
+    """The traffic counters stay attached to the kernel code they were taken
+    on: an edit of comments or blank space keeps the digest, a code edit
+    changes it, and a record with another digest is not reported."""
+    src = tmp_path / "k.hip"
+    base = "// header\nint f(int x) {\n    return x + 1;   // one\n}\n/* block\n comment */\n"
+    src.write_text(base)
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    d0 = bench.source_digest()
+    src.write_text("// other header\n\nint f(int x) {\n  return x + 1;\n}\n/* changed */\n")
+    assert bench.source_digest() == d0
+    src.write_text(base.replace("x + 1", "x + 2"))
+    d1 = bench.source_digest()
+    assert d1 != d0
+    rec = tmp_path / "traffic.json"
+    rec.write_text(json.dumps({"w": {"kernel_source_sha256_16": d1, "bytes_per_launch": 123}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    assert bench.read_traffic("w") == 123
+    src.write_text(base)
+    assert bench.read_traffic("w") is None
+    assert bench.read_traffic("missing") is None
